@@ -1,0 +1,268 @@
+"""Benchmark of the attention hot path on one MI355X; prints ONE JSON line.
+
+A step is one pass of the whole path over one batch of synthetic inputs:
+  1. prefill: causal GQA attention, B=2, Hq=32, Hkv=8, S=8192, d=128, bf16;
+  2. decode over a contiguous KV cache: B=64, Hq=32, Hkv=8, d=128, bf16,
+     cached lengths uniform in [512, 4096];
+  3. decode over a paged KV cache (16-token blocks, random physical placement,
+     per-sequence block table): B=16, Hq=32, Hkv=8, lengths in [8192, 32768].
+All inputs are resident in device memory before the timed region.  `value` is
+the prefill throughput in TFLOP/s (algorithmic FLOPs: 4*d*Hq*B per unmasked
+query-key pair); the decode KV bandwidth (every cached K/V byte read once)
+and tokens/s are reported beside it.  Per-kernel times come from HIP events
+recorded on the stream the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --only prefill|decode|paged --steps 3 --warmup 1   (profiling runs)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s + decode KV GB/s (GQA Hq=32 Hkv=8 d=128, bf16, 1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "paged"], default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_traffic(name: str, source_files):
+    """Per-launch HBM bytes measured by rocprofv3 counters, if still current.
+
+    Reads profiles/<name>_pmc.txt (written from two --pmc runs, FETCH_SIZE then
+    WRITE_SIZE, scaled by a plain copy's counters) and returns its bytes only
+    if the recorded source digest matches the kernel sources today.
+    """
+    import hashlib
+    path = os.path.join(PROFILES, f"{name}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^source_sha256:\s*(\w+)", text, re.M)
+    t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not t:
+        return None
+    h = hashlib.sha256()
+    for f in source_files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != m.group(1):
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline_prefill(w, q, k, v, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the prefill workload (whole heads)."""
+    import oracle
+    threads = os.environ.get("OMP_NUM_THREADS")
+    cores = int(threads) if threads else len(os.sched_getaffinity(0))
+    done_flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    hq = 0
+    while hq < w.Hq:
+        hk = oracle.kv_head_index(hq, w.Hq, w.Hkv)
+        qh = oracle.bf16_bits_to_f64(q[0, hq])
+        kh = oracle.bf16_bits_to_f64(k[0, hk])
+        vh = oracle.bf16_bits_to_f64(v[0, hk])
+        oracle.attention_head(qh, kh, vh, w.scale_value, w.causal)
+        done_flops += w.flops() / (w.B * w.Hq)
+        heads += 1
+        hq += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} whole query heads (b=0, heads 0..{heads - 1}) of the S=8192 causal GQA "
+                      f"prefill, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
+              "the attention path runs on a single device and multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_exact_attention_amd import gqa_attn
+    from transformer_exact_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gqa_attn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def gpu(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
+    do_paged = args.only in (None, "paged")
+
+    wp, wd, wpg = W.CFG3, W.CFG4, W.cfg5(8)
+    t_gen = time.perf_counter()
+    if do_prefill:
+        log(f"generating {wp.name}")
+        qp_np, kp_np, vp_np = W.prefill_inputs(wp)
+        qp, kp, vp = gpu(qp_np, "bf16"), gpu(kp_np, "bf16"), gpu(vp_np, "bf16")
+        op = torch.empty_like(qp)
+    if do_decode:
+        log(f"generating {wd.name}")
+        di = W.decode_inputs(wd)
+        dq, dk, dv = gpu(di.q, "bf16"), gpu(di.k_cache, "bf16"), gpu(di.v_cache, "bf16")
+        dl = gpu(di.seq_lens, "i32")
+        do_ = torch.empty_like(dq)
+        dws = gqa_attn.decode_workspace(wd.B, wd.Hq, wd.d, di.max_seq_len, dev)
+        d_bytes = W.decode_kv_bytes(di.seq_lens, wd.Hkv, wd.d)
+        del di
+    if do_paged:
+        log(f"generating {wpg.name}")
+        pi = W.decode_inputs(wpg)
+        pq, pk, pv = gpu(pi.q, "bf16"), gpu(pi.k_cache, "bf16"), gpu(pi.v_cache, "bf16")
+        pl, pt = gpu(pi.seq_lens, "i32"), gpu(pi.block_table, "i32")
+        po = torch.empty_like(pq)
+        p_max = pi.max_seq_len
+        pws = gqa_attn.decode_workspace(wpg.B, wpg.Hq, wpg.d, p_max, dev)
+        p_bytes = W.decode_kv_bytes(pi.seq_lens, wpg.Hkv, wpg.d)
+        del pi
+    torch.cuda.synchronize()
+    log(f"inputs resident on the GPU ({time.perf_counter() - t_gen:.1f} s)")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if do_prefill:
+            if ev: ev[0].record(stream)
+            gqa_attn.attn_prefill_fwd(qp, kp, vp, op, scale=wp.scale_value, causal=True, stream=stream)
+        if do_decode:
+            if ev: ev[1].record(stream)
+            gqa_attn.attn_decode_fwd(dq, dk, dv, dl, do_, scale=wd.scale_value, workspace=dws, stream=stream)
+        if do_paged:
+            if ev: ev[2].record(stream)
+            gqa_attn.attn_decode_fwd(pq, pk, pv, pl, po, block_table=pt, max_seq_len=p_max, scale=wpg.scale_value,
+                                     workspace=pws, stream=stream)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    def seg(a, b):
+        return np.array([ev[a].elapsed_time(ev[b]) for ev in events]) * 1e-3   # seconds
+
+    res = {}
+    # event pairs: prefill [0,1), decode [1,2), paged [2,3)
+    order = [n for n, on in (("prefill", do_prefill), ("decode", do_decode), ("paged", do_paged)) if on]
+    idx = {"prefill": 0, "decode": 1, "paged": 2}
+    for j, n in enumerate(order):
+        a = idx[n]
+        b = idx[order[j + 1]] if j + 1 < len(order) else 3
+        res[n] = seg(a, b)
+    ms_per_step = wall / args.steps * 1e3
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded iid N(0,1), bf16)"}
+    src_prefill = ["transformer_exact_attention_amd/csrc/prefill_bf16.hip",
+                   "transformer_exact_attention_amd/csrc/common.hpp"]
+    src_decode = ["transformer_exact_attention_amd/csrc/decode.hip",
+                  "transformer_exact_attention_amd/csrc/common.hpp",
+                  "transformer_exact_attention_amd/csrc/launch.hpp"]
+    if do_prefill:
+        t = float(np.mean(res["prefill"]))
+        tf = wp.flops() / t / 1e12
+        out.update({"value": round(tf, 2), "unit": "TFLOP/s"})
+        traffic = kernel_traffic("prefill_bf16_gqa_causal_B2_Hq32_Hkv8_S8192", src_prefill)
+        out["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                           "kernel": "prefill_bf16_kernel<128>",
+                           "algorithmic_flops_per_launch": wp.flops(),
+                           "algorithmic_bytes_per_launch": wp.io_bytes(),
+                           "avg_launch_us": round(t * 1e6, 2), "min_launch_us": round(float(np.min(res["prefill"])) * 1e6, 2)}
+    if do_decode:
+        t = float(np.mean(res["decode"]))
+        out["decode"] = {"workload": wd.name, "kv_bytes": d_bytes, "avg_call_us": round(t * 1e6, 2),
+                         "min_call_us": round(float(np.min(res["decode"])) * 1e6, 2),
+                         "kv_GBps": round(d_bytes / t / 1e9, 1), "tokens_per_s": round(wd.B / t, 1),
+                         "roofline": {"bound": "hbm", "achieved": round(d_bytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": round(d_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                                      "traffic": kernel_traffic("decode_gqa_contig_B64_Hq32_Hkv8", src_decode),
+                                      "note": "split + combine kernels, one call"}}
+    if do_paged:
+        t = float(np.mean(res["paged"]))
+        out["paged_decode"] = {"workload": wpg.name, "kv_bytes": p_bytes, "avg_call_us": round(t * 1e6, 2),
+                               "min_call_us": round(float(np.min(res["paged"])) * 1e6, 2),
+                               "kv_GBps": round(p_bytes / t / 1e9, 1), "tokens_per_s": round(wpg.B / t, 1),
+                               "roofline": {"bound": "hbm", "achieved": round(p_bytes / t / 1e9, 1),
+                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                            "frac": round(p_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                                            "traffic": kernel_traffic("decode_paged_B16_Hq32_Hkv8", src_decode)}}
+    if "value" not in out:
+        key = "decode" if do_decode else "paged_decode"
+        out.update({"value": out[key]["kv_GBps"], "unit": "GB/s"})
+        out["roofline"] = out[key]["roofline"]
+    out["config"] = {"workload": "step = causal GQA prefill B2 Hq32 Hkv8 S8192 d128 + contiguous GQA decode "
+                                 "B64 Hq32 Hkv8 L~U[512,4096] + paged GQA decode B16 Hq32 Hkv8 L~U[8192,32768]"
+                     if args.only is None else f"only {args.only}",
+                     "prefill": {"B": 2, "Hq": 32, "Hkv": 8, "S": 8192, "d": 128, "causal": True},
+                     "decode": {"B": 64, "Hq": 32, "Hkv": 8, "d": 128, "L": [512, 4096], "cache": "contiguous"},
+                     "paged_decode": {"B": 16, "Hq": 32, "Hkv": 8, "d": 128, "L": [8192, 32768], "block": 16}}
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+
+    if not args.no_cpu_baseline and do_prefill:
+        log("timing the fp64 oracle on a sample (CPU baseline)")
+        out["cpu_baseline"] = cpu_baseline_prefill(wp, qp_np, kp_np, vp_np)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+/*
+ * gqa_attn.h - C ABI of libgqa_attn: exact scaled-dot-product attention with
+ * grouped K/V heads (MHA when Hkv == Hq, GQA when 1 < Hkv < Hq, MQA when
+ * Hkv == 1) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For batch b and query head h, with g = Hq / Hkv and K/V
+ * head hk = floor(h / g):
+ *     O[b,h] = softmax(Q[b,h] K[b,hk]^T * scale) V[b,hk]
+ * [Different attention mechanisms (blog.gocoding.cloud), §1 MHA, step 3, for
+ * one head; §3 GQA, every N/G query heads share one K/V pair].  The grouping
+ * is contiguous: repeating every K/V head g times along the head axis
+ * [Attention variants deep-dive (devpress.csdn.net), §5 GQA code] gives
+ * query head h the K/V head floor(h / g); K/V are never copied per query head
+ * [same page, the note after the §5 code].  The result is exact attention
+ * computed tile by tile with an online softmax, so no Sq x Sk score matrix is
+ * ever written to device memory [Attention variants deep-dive, §6.2].
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; tensors are
+ *    dense, row-major, with the layouts stated per call.  The library never
+ *    allocates or frees memory and keeps no mutable global state; calls are
+ *    reentrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns before the kernels finish (except
+ *    attn_decode_validate, which synchronises).
+ *  - Every argument is checked on the host BEFORE any HIP call; a failed
+ *    check returns a status and enqueues nothing.  No C++ exception crosses
+ *    this boundary.
+ *  - dtype: GQA_F32 or GQA_BF16; q/k/v/o share it.  Accumulation, softmax
+ *    state and decode partials are always fp32.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, Hq % Hkv != 0, bad scale, ... */
+    GQA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head dim, dtype, group size) */
+    GQA_ERR_WORKSPACE = 3,     /* decode workspace missing or too small */
+    GQA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} gqa_status;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+#define GQA_ATTN_ABI_VERSION 1
+#define GQA_PAGE_BLOCK_SIZE 16   /* tokens per KV page */
+
+/* Version of this ABI (GQA_ATTN_ABI_VERSION of the built library). */
+int gqa_attn_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* gqa_attn_status_string(int status);
+
+/*
+ * Prefill / full attention forward.
+ *
+ *   q, o : [B, Hq,  Sq, d]      k, v : [B, Hkv, Sk, d]      (dtype elements)
+ *
+ * scale multiplies the scores q.k; pass 1/sqrt(d) for the pages' default
+ * [Attention variants deep-dive, §5 GQA code].  With causal != 0, key j is
+ * visible to query row i iff j <= i + (Sk - Sq) (the Sq queries are the last
+ * Sq positions; j <= i when Sq == Sk).
+ *
+ * Supported: d in {64, 128}; GQA_F32 (any group size g) and GQA_BF16 (g in
+ * {1, 2, 4, 8, 16, 32, 64, 128}).  Otherwise GQA_ERR_UNSUPPORTED.
+ * GQA_ERR_INVALID_ARG for: a NULL pointer, any size <= 0, Hq % Hkv != 0,
+ * causal with Sq > Sk, a non-finite or non-positive scale, a dtype outside
+ * gqa_dtype, or sizes whose element counts overflow 2^31 per (b, head) plane.
+ * o must not overlap q, k or v.
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                     float scale, int causal, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_fwd needs for these sizes (an upper
+ * bound valid for every Hkv dividing Hq).  0 on invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len);
+
+/*
+ * Decode: one new query token per sequence attends to its cached keys.
+ *
+ * Query b attends every cached key t in [0, seq_lens[b]) with no mask: its
+ * own K/V has already been appended at position seq_lens[b] - 1
+ * [Attention variants deep-dive, §7 KV Cache].  A sequence with length 0
+ * gets a zero output.
+ *
+ *   q, o      : [B, Hq, d]                                   (dtype elements)
+ *   seq_lens  : int32 [B], device, each in [0, max_seq_len]
+ *   block_table == NULL (contiguous cache):
+ *       k_cache, v_cache : [B, Hkv, max_seq_len, d]
+ *   block_table != NULL (paged cache, [Different attention mechanisms, §5
+ *   Page Attention: fixed-size blocks, per-sequence page table]):
+ *       k_cache, v_cache : [num_blocks, Hkv, block_size, d]
+ *       block_table      : int32 [B, max_blocks_per_seq], device; token t of
+ *                          sequence b lives in physical block
+ *                          block_table[b][t / block_size], slot t % block_size.
+ *                          Entries at or past ceil(seq_lens[b] / block_size)
+ *                          are never read.
+ *   workspace : device, >= attn_decode_workspace_bytes(B, Hq, d, max_seq_len)
+ *               bytes, 256-byte aligned; contents on entry are ignored.
+ *
+ * Supported: GQA_BF16, d == 128, block_size == GQA_PAGE_BLOCK_SIZE,
+ * g = Hq / Hkv in {1, 2, 4, 8, 16, 32}.
+ * GQA_ERR_INVALID_ARG for: a NULL pointer (block_table may be NULL), any size
+ * <= 0, Hq % Hkv != 0, a bad scale, paged with block_size != 16 or
+ * max_blocks_per_seq * block_size < max_seq_len.  GQA_ERR_WORKSPACE for a
+ * short or NULL workspace.  Device data (lengths, table entries in
+ * [0, num_blocks)) is the caller's contract: attn_decode_validate checks it.
+ */
+int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
+                    const int32_t* seq_lens, const int32_t* block_table,
+                    int B, int Hq, int Hkv, int d, int max_seq_len,
+                    int block_size, int max_blocks_per_seq,
+                    float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Debug/test helper (synchronous): copies seq_lens (and block_table, if not
+ * NULL) to the host and checks 0 <= seq_lens[b] <= max_seq_len and that every
+ * table entry a sequence reads lies in [0, num_physical_blocks).
+ * Returns GQA_OK, GQA_ERR_INVALID_ARG on bad data, GQA_ERR_HIP on a failed copy.
+ */
+int attn_decode_validate(const int32_t* seq_lens, const int32_t* block_table,
+                         int B, int max_seq_len, int block_size, int max_blocks_per_seq,
+                         int num_physical_blocks, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

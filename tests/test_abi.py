@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from transformer_exact_attention_amd import gqa_attn
+    return gqa_attn.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
+                            "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from transformer_exact_attention_amd import gqa_attn
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(gqa_attn.EXPORTS) == set(declared_functions())
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define GQA_ATTN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.gqa_attn_abi_version() == ver
+    for s in range(5):
+        assert lib.gqa_attn_status_string(s)
+    assert lib.gqa_attn_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000   # never dereferenced: every call below fails validation first
+
+
+def prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=4, Hkv=2, Sq=16, Sk=16, d=64, scale=0.125, causal=0,
+             dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(Hq=-1), 1), (dict(Sk=0), 1),
+    (dict(Hq=6, Hkv=4), 1),                  # query heads not a multiple of K/V heads
+    (dict(causal=1, Sq=17, Sk=16), 1),       # causal needs Sq <= Sk
+    (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=-1.0), 1),
+    (dict(dtype=7), 1),
+    (dict(d=96), 2), (dict(d=32), 2),
+    (dict(Hq=6, Hkv=2), 2),                  # bf16 group size 3 not supported
+    (dict(Sq=1 << 25, d=64), 1),             # plane element count overflow
+])
+def test_prefill_rejects_on_host(lib, kw, status):
+    assert prefill(lib, **kw) == status
+
+
+def decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, table=None, B=2, Hq=8, Hkv=2, d=128, max_seq_len=64,
+             block_size=0, max_blocks=0, scale=0.1, dtype=1, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_fwd(a["q"], a["k"], a["v"], a["o"], a["lens"], a["table"], a["B"], a["Hq"], a["Hkv"],
+                               a["d"], a["max_seq_len"], a["block_size"], a["max_blocks"], a["scale"], a["dtype"],
+                               a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lens=None), 1), (dict(B=0), 1), (dict(Hq=6, Hkv=4), 1), (dict(max_seq_len=0), 1),
+    (dict(scale=0.0), 1),
+    (dict(table=FAKE, block_size=8, max_blocks=8), 1),       # pages hold 16 tokens
+    (dict(table=FAKE, block_size=16, max_blocks=3), 1),      # 3 * 16 < max_seq_len
+    (dict(table=FAKE, block_size=16, max_blocks=0), 1),
+    (dict(d=64), 2), (dict(dtype=0), 2), (dict(Hq=128, Hkv=2), 2),   # g = 64 not supported for decode
+    (dict(ws=None), 3), (dict(ws=FAKE + 8), 3), (dict(ws_bytes=16), 3),
+])
+def test_decode_rejects_on_host(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_decode_workspace_formula(lib):
+    # fp32 partial outputs [B, Hq, nsplit, d] + fp32 LSE [B, Hq, nsplit], each 256-byte aligned
+    def expect(B, Hq, d, L, split=256):
+        ns = -(-L // split)
+        al = lambda x: (x + 255) // 256 * 256
+        return al(B * Hq * ns * d * 4) + al(B * Hq * ns * 4)
+    for args in [(64, 32, 128, 4096), (16, 32, 128, 32768), (1, 1, 128, 1), (3, 5, 128, 257)]:
+        assert lib.attn_decode_workspace_bytes(*args) == expect(*args)
+    assert lib.attn_decode_workspace_bytes(0, 32, 128, 10) == 0
+    assert lib.attn_decode_workspace_bytes(1, 32, 128, 0) == 0
+
+
+def test_validate_rejects_null(lib):
+    assert lib.attn_decode_validate(None, None, 1, 1, 0, 0, 0, None) == 1
+    assert lib.attn_decode_validate(FAKE, FAKE, 1, 16, 16, 0, 4, None) == 1
+
+
+def test_binding_raises_typed_errors_without_touching_the_gpu():
+    from transformer_exact_attention_amd import gqa_attn
+    with pytest.raises(ValueError):
+        gqa_attn._raise(1, "x")
+    with pytest.raises(NotImplementedError):
+        gqa_attn._raise(2, "x")
+    with pytest.raises(gqa_attn.GqaAttnError):
+        gqa_attn._raise(4, "x")
+    gqa_attn._raise(0, "x")

@@ -1,0 +1,215 @@
+"""Python binding of libgqa_attn (ctypes).
+
+Argument marshalling only: every step of attention runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  The functions
+carry the C names; tensors in, status codes turned into exceptions.
+
+The library is loaded from this package's directory.  If it is missing the
+first call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch  # noqa: F401  (loads the HIP runtime the library shares)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
+
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(5)
+GQA_F32, GQA_BF16 = 0, 1
+PAGE_BLOCK_SIZE = 16
+
+EXPORTS = ("gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
+           "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate")
+
+_lib = None
+
+
+class GqaAttnError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and type the C entry points.  Raises if the library is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libgqa_attn not built: {path} is missing "
+                          "(run `python -m transformer_exact_attention_amd.build`)")
+    lib = ctypes.CDLL(path)
+    c_int, c_float, c_size, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.gqa_attn_abi_version.restype = c_int
+    lib.gqa_attn_abi_version.argtypes = []
+    lib.gqa_attn_status_string.restype = ctypes.c_char_p
+    lib.gqa_attn_status_string.argtypes = [c_int]
+    lib.attn_prefill_fwd.restype = c_int
+    lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp] + [c_int] * 6 + [c_float, c_int, c_int, vp]
+    lib.attn_decode_workspace_bytes.restype = c_size
+    lib.attn_decode_workspace_bytes.argtypes = [c_int] * 4
+    lib.attn_decode_fwd.restype = c_int
+    lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, vp, c_size, vp]
+    lib.attn_decode_validate.restype = c_int
+    lib.attn_decode_validate.argtypes = [vp, vp] + [c_int] * 5 + [vp]
+    _lib = lib
+    return lib
+
+
+def gqa_attn_abi_version() -> int:
+    return load_library().gqa_attn_abi_version()
+
+
+def gqa_attn_status_string(status: int) -> str:
+    return load_library().gqa_attn_status_string(int(status)).decode()
+
+
+def _raise(status: int, what: str):
+    if status == GQA_OK:
+        return
+    msg = f"{what}: {gqa_attn_status_string(status)} (status {status})"
+    if status == GQA_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == GQA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise GqaAttnError(msg)
+
+
+_DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16}
+
+
+def _dtype_code(*ts) -> int:
+    dt = ts[0].dtype
+    if any(t.dtype != dt for t in ts):
+        raise ValueError("q/k/v/o must share one dtype")
+    if dt not in _DTYPES:
+        raise NotImplementedError(f"dtype {dt} not supported (float32, bfloat16)")
+    return _DTYPES[dt]
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None, *,
+                     scale: Optional[float] = None, causal: bool = False, stream=None) -> torch.Tensor:
+    """O = softmax(Q K^T * scale) V with grouped K/V heads; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d].
+
+    ``scale`` defaults to 1/sqrt(d).  Returns ``o`` (allocated when None).
+    """
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, d]")
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    if o is None:
+        o = torch.empty_like(q)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    _dev(q, k, v, o)
+    code = _dtype_code(q, k, v, o)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk, d,
+                              float(scale), 1 if causal else 0, code, _stream(stream))
+    _raise(st, "attn_prefill_fwd")
+    return o
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, d: int, max_seq_len: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, d, max_seq_len))
+
+
+def decode_workspace(B: int, Hq: int, d: int, max_seq_len: int, device="cuda") -> torch.Tensor:
+    """A byte tensor large enough for attn_decode_fwd (torch allocations are 256-byte aligned)."""
+    return torch.empty(attn_decode_workspace_bytes(B, Hq, d, max_seq_len), dtype=torch.uint8, device=device)
+
+
+def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                    o: Optional[torch.Tensor] = None, *, block_table: Optional[torch.Tensor] = None,
+                    max_seq_len: Optional[int] = None, scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One query token per sequence over a contiguous or paged KV cache.
+
+    q [B,Hq,d]; contiguous k/v_cache [B,Hkv,S_max,d]; paged k/v_cache
+    [num_blocks,Hkv,16,d] with block_table int32 [B,max_blocks].  seq_lens
+    int32 [B] on the device.  ``max_seq_len`` defaults to S_max (contiguous) or
+    16*max_blocks (paged).
+    """
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q must be [B,Hq,d]; k_cache and v_cache 4-D and equal in shape")
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[3] != d:
+        raise ValueError("head dim mismatch")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    tensors = [q, k_cache, v_cache, seq_lens]
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[2] != PAGE_BLOCK_SIZE:
+            raise ValueError("paged caches hold 16 tokens per block")
+        max_blocks = block_table.shape[1]
+        if max_seq_len is None:
+            max_seq_len = max_blocks * PAGE_BLOCK_SIZE
+        tensors.append(block_table)
+        bt_ptr = block_table.data_ptr()
+        block_size = PAGE_BLOCK_SIZE
+    else:
+        if k_cache.shape[0] != B:
+            raise ValueError("contiguous cache must be [B,Hkv,S_max,d]")
+        max_blocks = 0
+        block_size = 0
+        if max_seq_len is None:
+            max_seq_len = k_cache.shape[2]
+        if max_seq_len != k_cache.shape[2]:
+            raise ValueError("contiguous cache: max_seq_len must equal S_max")
+        bt_ptr = None
+    if o is None:
+        o = torch.empty_like(q)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    tensors.append(o)
+    _dev(*tensors)
+    code = _dtype_code(q, k_cache, v_cache, o)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, d, max_seq_len, q.device)
+    _dev(workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                             seq_lens.data_ptr(), bt_ptr, B, Hq, Hkv, d, int(max_seq_len), block_size,
+                             max_blocks, float(scale), code, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise(st, "attn_decode_fwd")
+    return o
+
+
+def attn_decode_validate(seq_lens: torch.Tensor, block_table: Optional[torch.Tensor], max_seq_len: int,
+                         num_physical_blocks: int = 0, stream=None) -> int:
+    """Synchronous check of device lengths / table entries; returns the status code."""
+    lib = load_library()
+    B = seq_lens.shape[0]
+    mb = block_table.shape[1] if block_table is not None else 0
+    bs = PAGE_BLOCK_SIZE if block_table is not None else 0
+    return lib.attn_decode_validate(seq_lens.data_ptr(), block_table.data_ptr() if block_table is not None else None,
+                                    B, int(max_seq_len), bs, mb, int(num_physical_blocks), _stream(stream))

@@ -8,7 +8,8 @@ random physical placement of 16-token KV blocks behind a per-sequence block
 table ([Different attention mechanisms, §5 Page Attention, steps 1-2]).
 
 Seeds: workload ``k`` draws stream ``s`` from ``numpy.random.default_rng([k, s])``
-with s = 0 (q), 1 (k), 2 (v), 3 (lengths), 4 (block permutation).
+(values: chunk ``i`` of 2^22 elements from ``default_rng([k, s, i])``) with
+s = 0 (q), 1 (k), 2 (v), 3 (lengths), 4 (block permutation).
 
 Everything is returned as numpy arrays: float32 for fp32 workloads, uint16
 bfloat16 bit patterns for bf16 workloads, int32 for lengths and tables.
@@ -16,6 +17,8 @@ bfloat16 bit patterns for bf16 workloads, int32 for lengths and tables.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -24,6 +27,7 @@ import numpy as np
 BLOCK_SIZE = 16          # tokens per KV page
 STREAM_Q, STREAM_K, STREAM_V, STREAM_LENS, STREAM_PERM = 0, 1, 2, 3, 4
 _CHUNK = 1 << 22
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 # ----------------------------------------------------------------------------
@@ -47,29 +51,42 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r
 
 
+def _fill_chunks(seed, n: int, out: np.ndarray, convert) -> None:
+    """Fill ``out`` (length n) chunk by chunk; chunk i draws from default_rng([*seed, i]).
+
+    Chunks are independent streams, so they are drawn on a few threads (numpy
+    releases the GIL while it fills an array).  The values depend only on the
+    seed and the fixed chunk size, never on the thread count.
+    """
+    seed = list(seed) if isinstance(seed, (list, tuple)) else [int(seed)]
+    starts = list(range(0, n, _CHUNK))
+
+    def one(i):
+        s = starts[i]
+        e = min(n, s + _CHUNK)
+        out[s:e] = convert(np.random.default_rng(seed + [i]).standard_normal(e - s, dtype=np.float32))
+
+    if len(starts) <= 1:
+        for i in range(len(starts)):
+            one(i)
+        return
+    with ThreadPoolExecutor(max_workers=min(_THREADS, len(starts))) as ex:
+        list(ex.map(one, range(len(starts))))
+
+
 def normal_f32(seed, shape) -> np.ndarray:
-    """iid N(0,1) float32 values of ``shape`` from ``default_rng(seed)``."""
-    rng = np.random.default_rng(seed)
+    """iid N(0,1) float32 values of ``shape`` (seed: int or list of ints)."""
     n = int(np.prod(shape, dtype=np.int64))
     out = np.empty(n, np.float32)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    _fill_chunks(seed, n, out, lambda x: x)
     return out.reshape(shape)
 
 
 def normal_bf16(seed, shape) -> np.ndarray:
-    """iid N(0,1) draws rounded to bfloat16; uint16 bit patterns of ``shape``.
-
-    Draws the same float32 stream as :func:`normal_f32` chunk by chunk, so the
-    peak host memory stays at one chunk of float32 beside the output.
-    """
-    rng = np.random.default_rng(seed)
+    """The same draws as :func:`normal_f32`, rounded to bfloat16; uint16 bit patterns."""
     n = int(np.prod(shape, dtype=np.int64))
     out = np.empty(n, np.uint16)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    _fill_chunks(seed, n, out, f32_to_bf16_bits)
     return out.reshape(shape)
 
 
