@@ -37,11 +37,11 @@ def inputs(seed, B, Hq, Hkv, Sq, Sk, d, dtype, qmul=1.0):
     return q, k, v
 
 
-def check_vs_oracle(ga, q, k, v, dtype, causal, scale=None, what=""):
+def check_vs_oracle(ga, q, k, v, dtype, causal, scale=None, what="", beyond_unit=False):
     note(f"prefill {what} q{q.shape} k{k.shape} {dtype} causal={causal}")
     o = run(ga, q, k, v, dtype, causal, scale)
     ref = oracle.attention(ref_f64(q, dtype), ref_f64(k, dtype), ref_f64(v, dtype), scale=scale, causal=causal)
-    return assert_close(to_f64(o), ref, dtype, what)
+    return assert_close(to_f64(o), ref, dtype, what, beyond_unit)
 
 
 # ----------------------------------------------------------------------------
@@ -84,7 +84,8 @@ def test_bf16_large_groups(ga, Hq, Hkv, S):
 @pytest.mark.parametrize("qmul", [8.0, 64.0])
 def test_bf16_peaked_softmax(ga, qmul):
     q, k, v = inputs(14, 1, 8, 2, 257, 257, 128, "bf16", qmul=qmul)
-    check_vs_oracle(ga, q, k, v, "bf16", True, None, f"peaked x{qmul}")
+    # near one-hot softmax: outputs approach single V rows (|O| up to ~4)
+    check_vs_oracle(ga, q, k, v, "bf16", True, None, f"peaked x{qmul}", beyond_unit=True)
 
 
 def test_bf16_explicit_scale(ga):

@@ -42,4 +42,18 @@ __device__ __forceinline__ float wave_shfl_xor(float x, int mask) {
     return __shfl_xor(x, mask, 64);
 }
 
+// Buffer resource over [base, base + bytes): raw (unswizzled) buffer loads
+// through it are range-checked by the hardware and return 0 past the end, so
+// ragged tiles need no branches.  Word 3 = 0x00020000 is the raw-buffer
+// format word of the CDNA3/CDNA4 generation.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// Wait for every outstanding memory operation of this wavefront.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 }  // namespace gqa

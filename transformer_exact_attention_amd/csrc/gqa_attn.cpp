@@ -43,7 +43,8 @@ int prefill_check(const void* q, const void* k, const void* v, void* o, int B, i
     if (dtype == GQA_BF16) {
         const int g = Hq / Hkv;
         if (!pow2(g) || g > 128) return GQA_ERR_UNSUPPORTED;
-        if (Hkv > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
+        // one workgroup per (query block, K/V head, batch entry) in a 1-D grid
+        if ((int64_t)Sq * Hkv * B >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
     } else {
         if (Hq > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
     }

@@ -31,12 +31,16 @@ struct DecodeArgs {
     void* workspace;
 };
 
-// Tokens of one decode split (one workgroup's share of a sequence).
-constexpr int kDecodeSplit = 256;
+// Tokens of one decode split (one workgroup's share of a sequence) are chosen
+// per call between kDecodeSplitMin and kDecodeSplitMax (powers of two).
+constexpr int kDecodeSplitMin = 256;
+constexpr int kDecodeSplitMax = 4096;
 
-// Workspace layout: fp32 partial outputs [B, Hq, nsplit_max, d], then fp32
-// log-sum-exp values [B, Hq, nsplit_max], each 256-byte aligned.
-inline int decode_nsplit_max(int max_seq_len) { return (max_seq_len + kDecodeSplit - 1) / kDecodeSplit; }
+// Workspace layout for split size T: fp32 partial outputs [B, Hq, ns, d] then
+// fp32 log-sum-exp values [B, Hq, ns], ns = ceil(max_seq_len / T), each
+// 256-byte aligned.  The size query uses T = kDecodeSplitMin: an upper bound.
+inline int decode_nsplit(int max_seq_len, int T) { return (max_seq_len + T - 1) / T; }
+inline int decode_nsplit_max(int max_seq_len) { return decode_nsplit(max_seq_len, kDecodeSplitMin); }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
     const size_t ns = (size_t)decode_nsplit_max(max_seq_len);

@@ -13,8 +13,9 @@
 //     ordered position-major (row r -> position p0 + r/g, head hk*g + r%g);
 //   * wavefront w owns rows 32w..32w+31; lane i owns query column n = i%32 and
 //     lane half hh = i/32 (the MFMA operand split along the contraction);
-//   * K/V tiles of 64 keys are staged in LDS once per workgroup and serve all
-//     128 rows (g query heads share them).
+//   * K/V tiles of 64 keys are staged row-major in LDS once per workgroup
+//     (double-buffered, one barrier per tile) and serve all 128 rows: the g
+//     query heads of a group share them.
 //
 // Per KV tile every wavefront computes the transposed score tile
 //   S^T (64 keys x 32 queries) = K (64 x d) . Q^T (d x 32)
@@ -22,10 +23,12 @@
 // running max / sum of a query live in that lane (and its partner i^32), and
 // only one cross-lane exchange per tile is needed.  The probabilities are then
 // already in the B-operand layout of
-//   O^T (d x 32 queries) += V^T (d x 64 keys) . P^T (64 keys x 32 queries)
-// provided V is stored transposed in LDS with the keys of each 16-key group
-// permuted to match the accumulator's row order; that transpose is done once
-// per tile per workgroup while staging.
+//   O^T (d x 32 queries) += V^T (d x 64 keys) . P^T (64 keys x 32 queries).
+// The V^T operand (8 keys of one d per lane) is read from the row-major V tile
+// with two transposing LDS reads (ds_read_b64_tr_b16): in each 16-lane group,
+// lane l receives element l%4 of the 8-byte pieces addressed by lanes l/4,
+// l/4+4, l/4+8, l/4+12, so pointing lane r of the group at key row r/4,
+// columns 4*(r%4).. gives lane l four keys of column l.
 //
 // Softmax runs in base 2: scores are multiplied by scale*log2(e) in fp32 and
 // exponentiated with v_exp_f32; exp(x) = 2^(x log2 e) changes only rounding.
@@ -40,42 +43,46 @@ namespace {
 constexpr int kBc = 64;        // keys per KV tile
 constexpr int kRowsWG = 128;   // query rows per workgroup
 constexpr int kThreads = 256;
+constexpr float kRescaleSlack = 8.0f;   // base-2 units: p <= 256 between rescales
 
-// LDS layouts (bf16 elements, 16-byte chunks XOR-swizzled against bank conflicts).
-//   Ks : [64 keys][D]   chunk c of row r stored at chunk c ^ (r & 7)
-//   Vt : [D][64 keys]   (keys permuted inside 16-key groups), chunk c of row r
-//                       stored at chunk c ^ ((r ^ (r >> 3)) & 7)
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// LDS tiles: K and V row-major [64 keys][D] bf16, 16-byte chunks XOR-swizzled
+// against bank conflicts for their read patterns:
+//   K: chunk c of key row r at chunk c ^ (r % chunks)    (reads: 32 rows, one chunk)
+//   V: chunk c of key row r at chunk c ^ ((4 * (r & 3)) % chunks)
+//      (transposing reads: 4 consecutive rows x 32 bytes per 16 lanes)
 template <int D>
 struct Lds {
     uint16_t ks[kBc * D];
-    uint16_t vt[D * kBc];
+    uint16_t vs[kBc * D];
 };
 
-__device__ __forceinline__ int ks_off(int D, int r, int chunk) {
-    return r * D + ((chunk ^ (r & 7)) << 3);
+template <int D>
+__device__ __forceinline__ int k_byte(int r, int chunk) {
+    return r * D * 2 + ((chunk ^ (r & (D / 8 - 1))) << 4);
 }
-__device__ __forceinline__ int vt_off(int r, int chunk) {
-    return r * kBc + ((chunk ^ ((r ^ (r >> 3)) & 7)) << 3);
+template <int D>
+__device__ __forceinline__ int v_byte(int r, int chunk) {
+    return r * D * 2 + ((chunk ^ ((4 * (r & 3)) & (D / 8 - 1))) << 4);
 }
-
-// Storage slot of the first key of 4-key group `sub` inside a 16-key group:
-// keys {0-3, 8-11 | 4-7, 12-15} so that lane half hh finds its 8 keys of a
-// 16-key MFMA step contiguous at slots 8*hh .. 8*hh+7.
-__device__ __forceinline__ int perm4(int sub) { return ((sub & 1) << 3) | ((sub & 2) << 1); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, int lg, int nqb,
     float scale_log2, int causal) {
-    constexpr int kChunks = D / 8;          // 16-byte chunks per K row
+    constexpr int kChunks = D / 8;          // 16-byte chunks per key row
     constexpr int kDSteps = D / 16;         // MFMA contraction steps over d
     constexpr int kDTiles = D / 32;         // 32-row output tiles of O^T
-    constexpr int kKLoads = kBc * kChunks / kThreads;        // K chunks per thread
-    constexpr int kVUnits = (kBc / 4) * kChunks;             // (4-key group, chunk) units
-    constexpr int kVLoads = (kVUnits + kThreads - 1) / kThreads;
+    constexpr int kLoads = kBc * kChunks / kThreads;   // 16-byte chunks per thread per tile (K and V each)
+    constexpr int kTileBytes = kBc * D * 2;
 
-    __shared__ Lds<D> lds;
+    __shared__ __attribute__((aligned(16))) Lds<D> ldsbuf[2];
+    lds_char* const lds0 = (lds_char*)&ldsbuf[0];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -85,10 +92,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int g = 1 << lg;
     const int P = kRowsWG >> lg;            // query positions per workgroup
 
-    // Heaviest (latest) query blocks first: causal rows there see the most keys.
-    const int qb = nqb - 1 - (int)blockIdx.x;
-    const int hk = blockIdx.y;
-    const int b = blockIdx.z;
+    // Work item of this workgroup.  Items are ordered plane by plane (plane =
+    // (batch, K/V head)), heaviest query block first within a plane.  The
+    // hardware hands consecutive workgroup ids to the 8 XCDs in turn, so
+    // workgroup id L runs on XCD L % 8; when the item count divides by 8, XCD x
+    // is given the contiguous item range [x * N/8, (x+1) * N/8): whole planes,
+    // whose K/V then stay in that XCD's L2 instead of being fetched by all 8.
+    const int nitems = (int)gridDim.x;
+    const int L = (int)blockIdx.x;
+    const int item = (nitems & 7) == 0 ? (L & 7) * (nitems >> 3) + (L >> 3) : L;
+    const int plane = item / nqb;
+    const int qb = nqb - 1 - (item - plane * nqb);
+    const int hk = plane % Hkv;
+    const int b = plane / Hkv;
     const int p0 = qb * P;
 
     // This lane's query column.
@@ -117,129 +133,115 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int my_last = causal ? pos + off : Sk - 1;          // last visible key of this column
     const int wg_first_last = causal ? min(p0 + off, Sk - 1) : Sk - 1;  // min over the workgroup
 
-    // Staging registers (next tile prefetch).
-    u32x4 kreg[kKLoads];
-    u32x4 vreg[kVLoads][4];
+    // K/V plane of this (batch, K/V head); keys past Sk read as zeros.
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(k + kvbase, (uint32_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + kvbase, (uint32_t)Sk * D * 2);
 
+    // Staging: thread covers chunk sc of rows srow + x * kRowStep, for K and V alike.
+    const int sc = tid % kChunks;
+    const int srow = tid / kChunks;
+    constexpr int kRowStep = kThreads / kChunks;
+    u32x4 kreg[kLoads], vreg[kLoads];
     auto load_tile = [&](int j0) {
 #pragma unroll
-        for (int x = 0; x < kKLoads; ++x) {
-            const int e = tid + x * kThreads;
-            const int row = e / kChunks, c = e % kChunks;
-            const int key = j0 + row;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (key < Sk) w = *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)key * D + 8 * c);
-            kreg[x] = w;
+        for (int x = 0; x < kLoads; ++x) {
+            const uint32_t eoff = (uint32_t)((j0 + srow + x * kRowStep) * D + 8 * sc) * 2;
+            kreg[x] = buffer_load16(krsrc, eoff);
+            vreg[x] = buffer_load16(vrsrc, eoff);
         }
+    };
+    auto store_tile = [&](int buf) {
+        lds_char* const base = lds0 + buf * (int)sizeof(Lds<D>);
 #pragma unroll
-        for (int x = 0; x < kVLoads; ++x) {
-            const int u = tid + x * kThreads;
-            const int g4 = u / kChunks, c = u % kChunks;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = j0 + 4 * g4 + rr;
-                u32x4 w = {0u, 0u, 0u, 0u};
-                if (u < kVUnits && key < Sk)
-                    w = *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)key * D + 8 * c);
-                vreg[x][rr] = w;
-            }
+        for (int x = 0; x < kLoads; ++x) {
+            const int row = srow + x * kRowStep;
+            *(lds_u32x4*)(base + k_byte<D>(row, sc)) = kreg[x];
+            *(lds_u32x4*)(base + kTileBytes + v_byte<D>(row, sc)) = vreg[x];
         }
     };
 
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int x = 0; x < kKLoads; ++x) {
-            const int e = tid + x * kThreads;
-            const int row = e / kChunks, c = e % kChunks;
-            *reinterpret_cast<u32x4*>(&lds.ks[ks_off(D, row, c)]) = kreg[x];
-        }
-#pragma unroll
-        for (int x = 0; x < kVLoads; ++x) {
-            const int u = tid + x * kThreads;
-            if (u < kVUnits) {
-                const int g4 = u / kChunks, c = u % kChunks;
-                const int slot = 16 * (g4 >> 2) + perm4(g4 & 3);     // first key's slot
-                const int chunk = slot >> 3, half = (slot >> 2) & 1;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int dw = e >> 1;
-                    u32x2 out;
-                    if (e & 1) {
-                        out.x = pack_hi16(vreg[x][0][dw], vreg[x][1][dw]);
-                        out.y = pack_hi16(vreg[x][2][dw], vreg[x][3][dw]);
-                    } else {
-                        out.x = pack_lo16(vreg[x][0][dw], vreg[x][1][dw]);
-                        out.y = pack_lo16(vreg[x][2][dw], vreg[x][3][dw]);
-                    }
-                    const int row = 8 * c + e;
-                    *reinterpret_cast<u32x2*>(&lds.vt[vt_off(row, chunk) + 4 * half]) = out;
-                }
-            }
-        }
-    };
+    // Transposed V reads: in 16-lane group G = lane/16, lane rr = lane%16 points
+    // at key row 16s + 4*(G/2) + 8*piece + rr/4 and column 32t + 16*(G%2) + 4*(rr%4).
+    const int G = lane >> 4, rr = lane & 15;
+    const int vrow0 = 4 * (G >> 1) + (rr >> 2);
+    const int vcol0 = 16 * (G & 1) + 4 * (rr & 3);
 
     f32x16 oacc[kDTiles];
 #pragma unroll
     for (int t = 0; t < kDTiles; ++t) oacc[t] = f32x16{};
-    float m = -INFINITY;     // running max (base-2 scaled units)
+    // Running reference max in scaled base-2 units.  It is raised only when a
+    // tile's max exceeds it by more than kRescaleSlack (then the accumulator
+    // and sum are rescaled); otherwise p = 2^(s*c - ref) <= 2^kRescaleSlack.
+    // Softmax does not depend on the reference, so this is exact up to
+    // rounding, and most tiles skip the O-accumulator rescale entirely.
+    float ref = -INFINITY;
     float l = 0.f;           // running sum over this lane's keys
 
-    if (ntiles > 0) load_tile(0);
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    // Nothing may stay in flight into the loop: the loop's first MFMA reads the
+    // Q fragments, and a load still pending there would make every iteration
+    // wait for the next tile's prefetch as well.
+    wait_all_memory();
+    __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
         const int j0 = kt * kBc;
-        __syncthreads();                      // previous tile fully consumed
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < ntiles) load_tile(j0 + kBc);
+        lds_char* const kb = lds0 + (kt & 1) * (int)sizeof(Lds<D>);
+        lds_char* const vb = kb + kTileBytes;
+        if (kt + 1 < ntiles) load_tile(j0 + kBc);        // in flight during this tile
 
-        // S^T = K . Q^T for keys j0 .. j0+63 (two 32-key tiles).
-        f32x16 sacc[2];
+        // S^T = K . Q^T for keys j0 .. j0+63 (two independent 32-key chains).
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            sacc[u] = f32x16{};
-            const int krow = 32 * u + n;
+        for (int t = 0; t < kDSteps; ++t) {
 #pragma unroll
-            for (int t = 0; t < kDSteps; ++t) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(&lds.ks[ks_off(D, krow, 2 * t + hh)]);
+            for (int u = 0; u < 2; ++u) {
+                const u32x4 w = *(lds_u32x4*)(kb + k_byte<D>(32 * u + n, 2 * t + hh));
                 sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[t],
                                                                    sacc[u], 0, 0, 0);
             }
         }
 
-        // Scale, mask, tile max.
-        const bool need_mask = (j0 + kBc - 1) > wg_first_last;
-        float tmax = -INFINITY;
+        // Mask (only tiles crossing the causal diagonal or the key end), tile max.
+        if ((j0 + kBc - 1) > wg_first_last) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float s = sacc[u][j] * scale_log2;
-                if (need_mask) {
+                for (int j = 0; j < 16; ++j) {
                     const int key = j0 + 32 * u + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    if (key > my_last) s = -INFINITY;
+                    if (key > my_last) sacc[u][j] = -INFINITY;
                 }
-                sacc[u][j] = s;
-                tmax = fmaxf(tmax, s);
-            }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m, tmax);
-        const float alpha = exp2_fast(m - m_new);      // 0 on the first tile (m = -inf)
-        m = m_new;
+        float tmax = sacc[0][0];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[u][j]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+        const bool raise = tmax > ref + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise)) {        // wave-uniform branch
+            const float ref_new = raise ? tmax : ref;
+            const float alpha = exp2_fast(ref - ref_new);  // 1 if kept, 0 on the first tile
+            ref = ref_new;
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < kDTiles; ++t) oacc[t] *= alpha;
+        }
 
-        // P = 2^(s - m), bf16 B-operand fragments for the four 16-key steps.
+        // P = 2^(s*c - ref), bf16 B-operand fragments for the four 16-key steps:
+        // step s = 2u + half holds keys 16s + {4hh..4hh+3, 8+4hh..8+4hh+3}.
         bf16x8 pf[4];
-        float psum = 0.f;
+        float psum4[4];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 float p[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2_fast(sacc[u][8 * half + e] - m_new);
-                    psum += p[e];
-                }
+                for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(sacc[u][8 * half + e], scale_log2, -ref));
+                psum4[2 * u + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
                 u32x4 w;
                 w.x = pack_bf16x2(p[0], p[1]);
                 w.y = pack_bf16x2(p[2], p[3]);
@@ -248,21 +250,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                 pf[2 * u + half] = __builtin_bit_cast(bf16x8, w);
             }
         }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) oacc[t] *= alpha;
+        l += (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
 
-        // O^T += V^T . P^T
+        // O^T += V^T . P^T; the A operand of (t, s) is two transposed reads:
+        // keys 16s + 4hh + 0..3 and 16s + 8 + 4hh + 0..3 of column 32t + n.
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const int vrow = 32 * t + n;
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(&lds.vt[vt_off(vrow, 2 * s + hh)]);
-                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[s],
-                                                                   oacc[t], 0, 0, 0);
+            for (int t = 0; t < kDTiles; ++t) {
+                const int col = 32 * t + vcol0;
+                const int row_a = 16 * s + vrow0;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(vb + v_byte<D>(row_a, col >> 3) + (col & 7) * 2));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(vb + v_byte<D>(row_a + 8, col >> 3) + (col & 7) * 2));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], oacc[t], 0, 0, 0);
             }
         }
+
+        if (kt + 1 < ntiles) store_tile((kt + 1) & 1);
+        __syncthreads();
     }
 
     // Epilogue: combine the lane pair's partial sums, normalise, store bf16.
@@ -292,7 +300,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     while ((1 << lg) < g) ++lg;
     const int P = kRowsWG >> lg;
     const int nqb = (a.Sq + P - 1) / P;
-    dim3 grid(nqb, a.Hkv, a.B);
+    dim3 grid(nqb * a.Hkv * a.B);
     const float sl = a.scale * kLog2e;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
