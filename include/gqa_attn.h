@@ -109,7 +109,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len);
  *               bytes, 256-byte aligned; contents on entry are ignored.
  *
  * Supported: GQA_BF16, d == 128, block_size == GQA_PAGE_BLOCK_SIZE,
- * g = Hq / Hkv in {1, 2, 4, 8, 16, 32}.
+ * g = Hq / Hkv in {1, 2, 4, 8, 16, 32}, B <= 4096.
  * GQA_ERR_INVALID_ARG for: a NULL pointer (block_table may be NULL), any size
  * <= 0, Hq % Hkv != 0, a bad scale, paged with block_size != 16 or
  * max_blocks_per_seq * block_size < max_seq_len.  GQA_ERR_WORKSPACE for a

@@ -84,6 +84,7 @@ def decode(lib, **kw):
     (dict(table=FAKE, block_size=16, max_blocks=3), 1),      # 3 * 16 < max_seq_len
     (dict(table=FAKE, block_size=16, max_blocks=0), 1),
     (dict(d=64), 2), (dict(dtype=0), 2), (dict(Hq=128, Hkv=2), 2),   # g = 64 not supported for decode
+    (dict(B=4097), 2),
     (dict(ws=None), 3), (dict(ws=FAKE + 8), 3), (dict(ws_bytes=16), 3),
 ])
 def test_decode_rejects_on_host(lib, kw, status):
@@ -91,11 +92,12 @@ def test_decode_rejects_on_host(lib, kw, status):
 
 
 def test_decode_workspace_formula(lib):
-    # fp32 partial outputs [B, Hq, nsplit, d] + fp32 LSE [B, Hq, nsplit], each 256-byte aligned
-    def expect(B, Hq, d, L, split=256):
-        ns = -(-L // split)
+    # fp32 partial outputs [B, Hq, P, d] + fp32 LSE [B, Hq, P] + int64 prefix sums [B + 1],
+    # each 256-byte aligned; P = ceil(L / 256) + 1 partials per (sequence, query head)
+    def expect(B, Hq, d, L, share=256):
+        P = -(-L // share) + 1
         al = lambda x: (x + 255) // 256 * 256
-        return al(B * Hq * ns * d * 4) + al(B * Hq * ns * 4)
+        return al(B * Hq * P * d * 4) + al(B * Hq * P * 4) + al((B + 1) * 8)
     for args in [(64, 32, 128, 4096), (16, 32, 128, 32768), (1, 1, 128, 1), (3, 5, 128, 257)]:
         assert lib.attn_decode_workspace_bytes(*args) == expect(*args)
     assert lib.attn_decode_workspace_bytes(0, 32, 128, 10) == 0

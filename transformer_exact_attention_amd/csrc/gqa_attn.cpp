@@ -69,8 +69,7 @@ int decode_check(const void* q, const void* kc, const void* vc, void* o, const i
     if (dtype != GQA_BF16 || d != 128) return GQA_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
     if (!pow2(g) || g > 32) return GQA_ERR_UNSUPPORTED;
-    const int ns = gqa::decode_nsplit_max(max_seq_len);
-    if (ns <= 0 || Hkv > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
+    if (B > gqa::kDecodeMaxBatch || Hq > 65535) return GQA_ERR_UNSUPPORTED;
     if (!workspace) return GQA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GQA_ERR_WORKSPACE;
     if (workspace_bytes < gqa::decode_workspace_bytes(B, Hq, d, max_seq_len)) return GQA_ERR_WORKSPACE;

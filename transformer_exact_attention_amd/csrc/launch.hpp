@@ -31,20 +31,38 @@ struct DecodeArgs {
     void* workspace;
 };
 
-// Tokens of one decode split (one workgroup's share of a sequence) are chosen
-// per call between kDecodeSplitMin and kDecodeSplitMax (powers of two).
-constexpr int kDecodeSplitMin = 256;
-constexpr int kDecodeSplitMax = 4096;
+// Decode work partition.  The flattened space of (sequence, K/V head, token)
+// triples, W = sum_b seq_lens[b] * Hkv tokens, is cut into equal consecutive
+// shares of Q tokens, one per wavefront (Q >= kDecodeMinShare, a multiple of
+// 16).  A share covering part of a (sequence, K/V head) segment produces one
+// partial result for that segment, so a segment of length L has at most
+// ceil(L / kDecodeMinShare) + 1 partials.
+constexpr int kDecodeMinShare = 256;
+constexpr int kDecodeMaxBatch = 4096;     // sequence prefix sums live in LDS
 
-// Workspace layout for split size T: fp32 partial outputs [B, Hq, ns, d] then
-// fp32 log-sum-exp values [B, Hq, ns], ns = ceil(max_seq_len / T), each
-// 256-byte aligned.  The size query uses T = kDecodeSplitMin: an upper bound.
-inline int decode_nsplit(int max_seq_len, int T) { return (max_seq_len + T - 1) / T; }
-inline int decode_nsplit_max(int max_seq_len) { return decode_nsplit(max_seq_len, kDecodeSplitMin); }
+inline int decode_max_partials(int max_seq_len) {
+    return (max_seq_len + kDecodeMinShare - 1) / kDecodeMinShare + 1;
+}
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout (each part 256-byte aligned):
+//   fp32 partial outputs [B, Hq, P, d], P = decode_max_partials(max_seq_len)
+//   fp32 base-2 log-sum-exp [B, Hq, P]
+//   int64 token prefix sums over sequences [B + 1]
+struct DecodeWorkspace {
+    size_t part_o, part_lse, prefix, total;
+};
+inline DecodeWorkspace decode_workspace_layout(int B, int Hq, int d, int max_seq_len) {
+    const size_t P = (size_t)decode_max_partials(max_seq_len);
+    DecodeWorkspace w;
+    w.part_o = 0;
+    w.part_lse = align256((size_t)B * Hq * P * d * 4);
+    w.prefix = w.part_lse + align256((size_t)B * Hq * P * 4);
+    w.total = w.prefix + align256((size_t)(B + 1) * 8);
+    return w;
+}
 inline size_t decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
-    const size_t ns = (size_t)decode_nsplit_max(max_seq_len);
-    return align256((size_t)B * Hq * ns * d * 4) + align256((size_t)B * Hq * ns * 4);
+    return decode_workspace_layout(B, Hq, d, max_seq_len).total;
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
