@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode", "paged"], default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload separately (one JSON line each) instead of the step")
     return ap.parse_args()
 
 
@@ -101,6 +103,83 @@ def cpu_baseline_prefill(w, q, k, v, budget_s=12.0):
                       f"prefill, fp64 numpy, {dt:.1f} s"}
 
 
+def sweep(args):
+    """Every workload on its own: prefill (fp32 tiny, MHA S2048, GQA S8192), contiguous
+    decode, paged decode with Hkv in {32, 8, 1}.  One JSON line per workload."""
+    import torch
+    from transformer_exact_attention_amd import gqa_attn
+    from transformer_exact_attention_amd import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def gpu(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for w in (W.CFG1, W.CFG2, W.CFG3):
+        log(f"sweep {w.name}")
+        q, k, v = (gpu(x, w.dtype) for x in W.prefill_inputs(w))
+        o = torch.empty_like(q)
+        t = timed(lambda: gqa_attn.attn_prefill_fwd(q, k, v, o, scale=w.scale_value, causal=w.causal,
+                                                    stream=stream), args.steps)
+        tf = w.flops() / float(np.mean(t)) / 1e12
+        print(json.dumps({"workload": w.name, "kind": "prefill", "dtype": w.dtype, "avg_us": round(float(np.mean(t)) * 1e6, 2),
+                          "min_us": round(float(np.min(t)) * 1e6, 2), "TFLOPs": round(tf, 2),
+                          "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4) if w.dtype == "bf16" else None}),
+              flush=True)
+        del q, k, v, o
+    for w in (W.CFG4, W.cfg5(32), W.cfg5(8), W.cfg5(1)):
+        log(f"sweep {w.name}")
+        di = W.decode_inputs(w)
+        q, kc, vc = gpu(di.q, "bf16"), gpu(di.k_cache, "bf16"), gpu(di.v_cache, "bf16")
+        lens = gpu(di.seq_lens, "i32")
+        bt = gpu(di.block_table, "i32") if w.paged else None
+        o = torch.empty_like(q)
+        ws = gqa_attn.decode_workspace(w.B, w.Hq, w.d, di.max_seq_len, dev)
+        nbytes = W.decode_kv_bytes(di.seq_lens, w.Hkv, w.d)
+        del di
+
+        def call():
+            flush.fill_(1)                      # evict the 256 MB Infinity Cache before every call
+            gqa_attn.attn_decode_fwd(q, kc, vc, lens, o, block_table=bt, max_seq_len=None if not w.paged else
+                                     w.max_blocks * W.BLOCK_SIZE, scale=w.scale_value, workspace=ws, stream=stream)
+        ev = []
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            gqa_attn.attn_decode_fwd(q, kc, vc, lens, o, block_table=bt, max_seq_len=None if not w.paged else
+                                     w.max_blocks * W.BLOCK_SIZE, scale=w.scale_value, workspace=ws, stream=stream)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        gbs = nbytes / float(np.mean(t)) / 1e9
+        print(json.dumps({"workload": w.name, "kind": "decode", "kv_bytes": nbytes,
+                          "avg_us": round(float(np.mean(t)) * 1e6, 2), "min_us": round(float(np.min(t)) * 1e6, 2),
+                          "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                          "tokens_per_s": round(w.B / float(np.mean(t)), 1)}), flush=True)
+        del q, kc, vc, lens, bt, o, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +198,9 @@ def main():
     gqa_attn.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        sweep(args)
+        return
 
     def gpu(a, kind):
         if kind == "bf16":
