@@ -27,6 +27,12 @@ HOST_SOURCES = ["gqa_attn.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-ffp-contract=fast"]
+# Per-source extras.  The bf16 prefill kernel keeps its output accumulators in
+# AGPRs through inline asm and needs every compiler-generated MFMA (the score
+# product, read by the softmax) in the VGPR form.
+SOURCE_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Sources whose generated assembly must pass asm_check (MFMAs in inline asm).
+ASM_CHECKED = ["prefill_bf16.hip"]
 
 
 def hipcc() -> str:
@@ -67,13 +73,28 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append((obj, [cc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [cc, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                           "-o", obj]))
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append((obj, [cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c",
                            os.path.join(CSRC, src), "-o", obj]))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        outs = list(ex.map(lambda j: _run(j[1]), jobs))
+    # Assembly of the sources with inline-asm MFMAs, for the hazard check.
+    asm_jobs = []
+    for src in ASM_CHECKED:
+        out = os.path.join(BUILD_DIR, src + ".s")
+        asm_jobs.append((out, [cc, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S",
+                               os.path.join(CSRC, src), "-o", out]))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs) + len(asm_jobs))) as ex:
+        outs = list(ex.map(lambda j: _run(j[1]), jobs + asm_jobs))[:len(jobs)]
+    try:
+        from . import asm_check
+    except ImportError:          # run as a script: this directory is on sys.path
+        import asm_check
+    for out, _ in asm_jobs:
+        problems = asm_check.check(open(out).read())
+        if problems:
+            raise RuntimeError(f"MFMA wait-state check failed for {out}:\n" + "\n".join(problems))
     if verbose:
         for (obj, cmd), out in zip(jobs, outs):
             print(" ".join(cmd))

@@ -7,82 +7,157 @@
 // Query head h reads K/V head h / g [Attention variants deep-dive, §5 GQA
 // code], without copying K/V per query head (§5, the note after the code).
 //
-// Work decomposition (one workgroup = 4 wavefronts = 256 lanes):
-//   * a workgroup owns one K/V head of one batch entry and 128 "query rows":
-//     P = 128/g consecutive query positions x all g query heads of the group,
+// Work decomposition (one workgroup = 4 wavefronts, one workgroup per CU):
+//   * a workgroup owns one K/V head of one batch entry and 256 "query rows":
+//     256/g consecutive query positions x all g query heads of the group,
 //     ordered position-major (row r -> position p0 + r/g, head hk*g + r%g);
-//   * wavefront w owns rows 32w..32w+31; lane i owns query column n = i%32 and
-//     lane half hh = i/32 (the MFMA operand split along the contraction);
-//   * K/V tiles of 64 keys are staged row-major in LDS once per workgroup
-//     (double-buffered, one barrier per tile) and serve all 128 rows: the g
-//     query heads of a group share them.
+//   * wavefront w owns rows 64w..64w+63 as two 32-row blocks nb = 0, 1; lane i
+//     owns query column i%32 of each block and lane half hh = i/32 (the MFMA
+//     operand split along the contraction);
+//   * the Q rows are staged in LDS once; K/V tiles of 64 keys are staged in
+//     LDS by direct-to-LDS buffer loads, three buffers each (Q and the six
+//     tiles fill the 160 KB LDS), and serve all 256 rows: the g query heads
+//     of a group share them.  The step that computes the scores of tile j+1
+//     loads K tile j+2 and V tile j+1, spread over its first half so that the
+//     four wavefronts do not queue 32 KB of requests at once.
 //
 // Per KV tile every wavefront computes the transposed score tile
-//   S^T (64 keys x 32 queries) = K (64 x d) . Q^T (d x 32)
-// so the 32x32 accumulator layout puts one query column in each lane: the
-// running max / sum of a query live in that lane (and its partner i^32), and
-// only one cross-lane exchange per tile is needed.  The probabilities are then
-// already in the B-operand layout of
-//   O^T (d x 32 queries) += V^T (d x 64 keys) . P^T (64 keys x 32 queries).
+//   S^T (64 keys x 64 queries) = K (64 x d) . Q^T (d x 64)
+// so the 32x32 accumulator layout puts one query column in each lane and a
+// query's softmax state lives in that lane (and its partner i^32).  The
+// probabilities are then already in the B-operand layout of
+//   O^T (d x 64 queries) += V^T (d x 64 keys) . P^T (64 keys x 64 queries).
 // The V^T operand (8 keys of one d per lane) is read from the row-major V tile
 // with two transposing LDS reads (ds_read_b64_tr_b16): in each 16-lane group,
 // lane l receives element l%4 of the 8-byte pieces addressed by lanes l/4,
 // l/4+4, l/4+8, l/4+12, so pointing lane r of the group at key row r/4,
-// columns 4*(r%4).. gives lane l four keys of column l.
+// columns 4*(r%4).. gives lane l four keys of column l.  Holding 64 query
+// columns per wavefront makes every LDS operand read feed two MFMAs.
+//
+// Software pipeline.  While the softmax of tile j runs on the vector ALU, the
+// matrix cores compute the scores of tile j+1 and the P.V product of tile
+// j-1, so the exponentials overlap matrix work instead of alternating with it.
 //
 // Softmax runs in base 2: scores are multiplied by scale*log2(e) in fp32 and
 // exponentiated with v_exp_f32; exp(x) = 2^(x log2 e) changes only rounding.
-// P is rounded to bf16 for the PV product; accumulation is fp32 throughout.
+// The reference point of the exponent is raised lazily: p = 2^(s*c - ref)
+// with ref a past running max; a tile is redone against its true max (and the
+// accumulator and sum rescaled) only when some lane's tile sum of p exceeds
+// 2^8, which bounds every p by 2^8.  Softmax does not depend on the reference
+// point, so the result is exact up to rounding.  P is rounded to bf16 for the
+// PV product and the row sums add exactly those rounded values (v_dot2 with
+// fp32 accumulation); accumulation is fp32 throughout.
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace gqa {
 
 namespace {
 
-constexpr int kBc = 64;        // keys per KV tile
-constexpr int kRowsWG = 128;   // query rows per workgroup
-constexpr int kThreads = 256;
-constexpr float kRescaleSlack = 8.0f;   // base-2 units: p <= 256 between rescales
+constexpr int kBc = 64;                  // keys per KV tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsWG = 64 * kWaves;     // query rows per workgroup
+constexpr float kSumLimit = 256.0f;      // 2^8: per-lane tile sum of p that forces a rescale
 
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// LDS tiles: K and V row-major [64 keys][D] bf16, 16-byte chunks XOR-swizzled
+// LDS tiles are row-major [rows][D] bf16 with 16-byte chunks XOR-swizzled
 // against bank conflicts for their read patterns:
-//   K: chunk c of key row r at chunk c ^ (r % chunks)    (reads: 32 rows, one chunk)
-//   V: chunk c of key row r at chunk c ^ ((4 * (r & 3)) % chunks)
-//      (transposing reads: 4 consecutive rows x 32 bytes per 16 lanes)
+//   Q, K: chunk c of row r at chunk c ^ (r % chunks)   (reads: 32 rows, one chunk)
+//   V:    chunk c of row r at chunk c ^ ((4 * (r & 3)) % chunks)
+//         (transposing reads: 4 consecutive rows x 32 bytes per 16 lanes)
 template <int D>
-struct Lds {
-    uint16_t ks[kBc * D];
-    uint16_t vs[kBc * D];
-};
+__device__ __forceinline__ int k_swz(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int k_byte(int r, int chunk) { return r * D * 2 + ((chunk ^ k_swz<D>(r)) << 4); }
+template <int D>
+__device__ __forceinline__ int v_byte(int r, int chunk) { return r * D * 2 + ((chunk ^ v_swz<D>(r)) << 4); }
+
+// O^T accumulation in AGPRs.  The compiler would otherwise give every MFMA
+// the same register file, and the score accumulators, which the softmax reads
+// with vector instructions, must stay in VGPRs.  The compiler does not see
+// into the asm, so it cannot supply the two wait states an MFMA needs after a
+// vector instruction wrote its A/B operands: the build checks the generated
+// code for that (asm_check.py).  Back to back on the same accumulator the
+// MFMA needs none.  Code that reads the accumulator afterwards first passes
+// through agpr_settle().
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Workgroup barrier without a memory fence.  Every wavefront first waits for
+// its own direct-to-LDS loads whose data the others are about to read; a
+// fenced barrier would also wait for the loads still meant to be in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most N LDS operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
+// Wait states between the last MFMA that wrote an accumulator and a vector
+// instruction reading it (more than the 8-pass MFMA's result latency).
+template <int N>
+__device__ __forceinline__ void agpr_settle(f32x16 (&acc)[2][N]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int t = 0; t < N; ++t) asm volatile("" : "+a"(acc[nb][t]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int t = 0; t < N; ++t) asm volatile("" : "+a"(acc[nb][t]));
+}
+
+__device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
+}
 
 template <int D>
-__device__ __forceinline__ int k_byte(int r, int chunk) {
-    return r * D * 2 + ((chunk ^ (r & (D / 8 - 1))) << 4);
-}
-template <int D>
-__device__ __forceinline__ int v_byte(int r, int chunk) {
-    return r * D * 2 + ((chunk ^ ((4 * (r & 3)) & (D / 8 - 1))) << 4);
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, int lg, int nqb,
     float scale_log2, int causal) {
-    constexpr int kChunks = D / 8;          // 16-byte chunks per key row
-    constexpr int kDSteps = D / 16;         // MFMA contraction steps over d
-    constexpr int kDTiles = D / 32;         // 32-row output tiles of O^T
-    constexpr int kLoads = kBc * kChunks / kThreads;   // 16-byte chunks per thread per tile (K and V each)
-    constexpr int kTileBytes = kBc * D * 2;
+    constexpr int kChunks = D / 8;                          // 16-byte chunks per row
+    constexpr int kDSteps = D / 16;                         // MFMA contraction steps over d
+    constexpr int kDTiles = D / 32;                         // 32-row output tiles of O^T
+    constexpr int kTileLoads = kBc * kChunks / 64 / kWaves; // 1 KB direct loads per wavefront per tile
+    constexpr int kQLoads = kRowsWG * kChunks / 64 / kWaves;
+    constexpr int kStepsPerWindow = kDSteps / 4;            // score steps per pipeline window
 
-    __shared__ __attribute__((aligned(16))) Lds<D> ldsbuf[2];
-    lds_char* const lds0 = (lds_char*)&ldsbuf[0];
+    // Separate arrays, so that the compiler can tell the buffers being filled
+    // by direct loads from the ones being read.
+    __shared__ __attribute__((aligned(1024))) uint16_t q_s[kRowsWG * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s0[kBc * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s1[kBc * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s2[kBc * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s0[kBc * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s1[kBc * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s2[kBc * D];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -90,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int n = lane & 31;
     const int hh = lane >> 5;
     const int g = 1 << lg;
-    const int P = kRowsWG >> lg;            // query positions per workgroup
+    const int npos = kRowsWG >> lg;         // query positions per workgroup
 
     // Work item of this workgroup.  Items are ordered plane by plane (plane =
     // (batch, K/V head)), heaviest query block first within a plane.  The
@@ -105,189 +180,453 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int qb = nqb - 1 - (item - plane * nqb);
     const int hk = plane % Hkv;
     const int b = plane / Hkv;
-    const int p0 = qb * P;
-
-    // This lane's query column.
-    const int r = wave * 32 + n;
-    const int pos = p0 + (r >> lg);
-    const int head = hk * g + (r & (g - 1));
-    const bool qlive = pos < Sq;
+    const int p0 = qb * npos;
     const int off = Sk - Sq;                // causal: key j visible iff j <= pos + off
 
-    const size_t qrow = (((size_t)b * Hq + head) * Sq + (qlive ? pos : 0)) * D;
-    const size_t kvbase = ((size_t)b * Hkv + hk) * (size_t)Sk * D;
-
-    // Q^T operand fragments: lane holds Q[query n][16t + 8hh .. +8].
-    bf16x8 qf[kDSteps];
+    // Last visible key of this lane's two query columns.
+    int my_last[2];
 #pragma unroll
-    for (int t = 0; t < kDSteps; ++t) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (qlive) w = *reinterpret_cast<const u32x4*>(q + qrow + 16 * t + 8 * hh);
-        qf[t] = __builtin_bit_cast(bf16x8, w);
+    for (int nb = 0; nb < 2; ++nb) {
+        const int r = 64 * wave + 32 * nb + n;
+        my_last[nb] = causal ? p0 + (r >> lg) + off : Sk - 1;
     }
 
-    // Keys this workgroup needs.
-    const int p_last = min(p0 + P, Sq) - 1;
+    // Keys this workgroup needs; tiles past the wavefront's first diagonal key need the mask.
+    const int p_last = min(p0 + npos, Sq) - 1;
     const int kend = causal ? min(Sk, p_last + off + 1) : Sk;
     const int ntiles = (kend + kBc - 1) / kBc;
-    const int my_last = causal ? pos + off : Sk - 1;          // last visible key of this column
-    const int wg_first_last = causal ? min(p0 + off, Sk - 1) : Sk - 1;  // min over the workgroup
+    const int wave_first_last = causal ? min(p0 + ((64 * wave) >> lg) + off, Sk - 1) : Sk - 1;
 
-    // K/V plane of this (batch, K/V head); keys past Sk read as zeros.
-    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(k + kvbase, (uint32_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + kvbase, (uint32_t)Sk * D * 2);
-
-    // Staging: thread covers chunk sc of rows srow + x * kRowStep, for K and V alike.
-    const int sc = tid % kChunks;
-    const int srow = tid / kChunks;
-    constexpr int kRowStep = kThreads / kChunks;
-    u32x4 kreg[kLoads], vreg[kLoads];
-    auto load_tile = [&](int j0) {
+    // ---- staging -------------------------------------------------------
+    // A direct load moves 16 bytes per lane into consecutive LDS slots
+    // (lane i -> slot base + i), so each lane fetches the global chunk whose
+    // swizzled place is its slot.  The buffer resources end at key kend:
+    // keys past it (the rest of the last tile, and the tiles past the last
+    // that the final steps address) are not fetched.  The K/V tiles are
+    // zero-filled once, so such rows hold zeros or an older tile's finite
+    // values, and the mask removes them.
+    const size_t kvbase = ((size_t)b * Hkv + hk) * (size_t)Sk * D;
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(k + kvbase, (uint32_t)kend * D * 2);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + kvbase, (uint32_t)kend * D * 2);
+    // Load x of wavefront w fills the 1 KB slot group t = 4x + w, i.e. rows
+    // (64 t + lane) / chunks.  Every row of load x is 16x (d = 128) or 32x
+    // (d = 64) rows past that of load 0, a multiple of the swizzle period, so
+    // a lane fetches the same chunk column in all its loads and its byte
+    // offset is one base plus 4096 x.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform LDS bases
+    uint32_t st_kbase, st_vbase;
+    {
+        const int s = 64 * wave + lane;
+        const int row = s / kChunks, pp = s % kChunks;
+        st_kbase = (uint32_t)(row * D * 2 + 16 * (pp ^ k_swz<D>(row)));
+        st_vbase = (uint32_t)(row * D * 2 + 16 * (pp ^ v_swz<D>(row)));
+    }
+    auto issue_load = [&](__amdgpu_buffer_rsrc_t r, uint32_t vbase, uint16_t* dst, int tile, int x) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void*)((lds_char*)(dst) + 1024 * (4 * x + wave_u)), 16,
+            vbase + (uint32_t)(tile * (kBc * D * 2) + 4096 * x), 0, 0, 0);
+    };
+    auto issue_tile = [&](__amdgpu_buffer_rsrc_t r, uint32_t vbase, uint16_t* dst, int tile) {
 #pragma unroll
-        for (int x = 0; x < kLoads; ++x) {
-            const uint32_t eoff = (uint32_t)((j0 + srow + x * kRowStep) * D + 8 * sc) * 2;
-            kreg[x] = buffer_load16(krsrc, eoff);
-            vreg[x] = buffer_load16(vrsrc, eoff);
+        for (int x = 0; x < kTileLoads; ++x) issue_load(r, vbase, dst, tile, x);
+    };
+
+    // Q rows of the workgroup -> LDS, once, through registers (16-byte
+    // chunks, same swizzle as K).  Ordinary loads keep the compiler's
+    // tracking of direct-to-LDS targets to the K/V buffers of the loop.
+    {
+        const uint16_t* qgroup = q + ((size_t)b * Hq + (size_t)hk * g) * (size_t)Sq * D;
+        constexpr int kBatch = kQLoads;
+#pragma unroll
+        for (int x0 = 0; x0 < kQLoads; x0 += kBatch) {
+            u32x4 qv[kBatch];
+#pragma unroll
+            for (int x = 0; x < kBatch; ++x) {
+                const int row = (tid + kThreads * (x0 + x)) / kChunks;
+                const int c = (tid + kThreads * (x0 + x)) % kChunks;
+                const int prow = min(p0 + (row >> lg), Sq - 1);
+                qv[x] = *reinterpret_cast<const u32x4*>(qgroup + ((size_t)(row & (g - 1)) * Sq + prow) * D + 8 * c);
+            }
+#pragma unroll
+            for (int x = 0; x < kBatch; ++x) {
+                const int row = (tid + kThreads * (x0 + x)) / kChunks;
+                const int c = (tid + kThreads * (x0 + x)) % kChunks;
+                *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(row, c)) = qv[x];
+            }
+        }
+    }
+    // Zero the K/V tiles (the first step also multiplies a zero P by V
+    // buffer 2), then start K tiles 0, 1 and V tile 0.
+    for (int i = tid; i < kBc * D / 8; i += kThreads) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        ((lds_u32x4*)(lds_char*)k_s0)[i] = z;
+        ((lds_u32x4*)(lds_char*)k_s1)[i] = z;
+        ((lds_u32x4*)(lds_char*)k_s2)[i] = z;
+        ((lds_u32x4*)(lds_char*)v_s0)[i] = z;
+        ((lds_u32x4*)(lds_char*)v_s1)[i] = z;
+        ((lds_u32x4*)(lds_char*)v_s2)[i] = z;
+    }
+    __syncthreads();
+    issue_tile(krsrc, st_kbase, k_s0, 0);
+    issue_tile(krsrc, st_kbase, k_s1, 1);
+    issue_tile(vrsrc, st_vbase, v_s0, 0);
+
+    // ---- operand reads -------------------------------------------------
+    const int qrow0 = 64 * wave + n;
+    auto qk_step = [&](const uint16_t* ks, f32x16 (&sacc)[2][2], int t, bool first) {
+        const u32x4 a0 = *(lds_u32x4*)((lds_char*)ks + k_byte<D>(n, 2 * t + hh));
+        const u32x4 a1 = *(lds_u32x4*)((lds_char*)ks + k_byte<D>(32 + n, 2 * t + hh));
+        const u32x4 b0 = *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(qrow0, 2 * t + hh));
+        const u32x4 b1 = *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(qrow0 + 32, 2 * t + hh));
+        const f32x16 z = {};
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const bf16x8 bq = __builtin_bit_cast(bf16x8, nb ? b1 : b0);
+            sacc[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), bq,
+                                                                  first ? z : sacc[nb][0], 0, 0, 0);
+            sacc[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), bq,
+                                                                  first ? z : sacc[nb][1], 0, 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
-        lds_char* const base = lds0 + buf * (int)sizeof(Lds<D>);
-#pragma unroll
-        for (int x = 0; x < kLoads; ++x) {
-            const int row = srow + x * kRowStep;
-            *(lds_u32x4*)(base + k_byte<D>(row, sc)) = kreg[x];
-            *(lds_u32x4*)(base + kTileBytes + v_byte<D>(row, sc)) = vreg[x];
-        }
-    };
-
     // Transposed V reads: in 16-lane group G = lane/16, lane rr = lane%16 points
     // at key row 16s + 4*(G/2) + 8*piece + rr/4 and column 32t + 16*(G%2) + 4*(rr%4).
     const int G = lane >> 4, rr = lane & 15;
     const int vrow0 = 4 * (G >> 1) + (rr >> 2);
     const int vcol0 = 16 * (G & 1) + 4 * (rr & 3);
-
-    f32x16 oacc[kDTiles];
+    auto pv_step = [&](const uint16_t* vs, f32x16 (&oacc)[2][kDTiles], const bf16x8 (&pf)[2][4], int s) {
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t) oacc[t] = f32x16{};
-    // Running reference max in scaled base-2 units.  It is raised only when a
-    // tile's max exceeds it by more than kRescaleSlack (then the accumulator
-    // and sum are rescaled); otherwise p = 2^(s*c - ref) <= 2^kRescaleSlack.
-    // Softmax does not depend on the reference, so this is exact up to
-    // rounding, and most tiles skip the O-accumulator rescale entirely.
-    float ref = -INFINITY;
-    float l = 0.f;           // running sum over this lane's keys
+        for (int t = 0; t < kDTiles; ++t) {
+            const int col = 32 * t + vcol0;
+            const int row_a = 16 * s + vrow0;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((lds_char*)vs + v_byte<D>(row_a, col >> 3) + (col & 7) * 2));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((lds_char*)vs + v_byte<D>(row_a + 8, col >> 3) + (col & 7) * 2));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                mfma_agpr(oacc[nb][t], a, pf[nb][s]);
+        }
+    };
+    // P block (nb, kb) = 2^(s*c - ref) as bf16 B-operand fragments for the
+    // 16-key steps 2kb, 2kb+1 (step s holds keys 16s + {4hh..4hh+3,
+    // 8+4hh..8+4hh+3}), plus their sum.
+    auto softmax_block = [&](const f32x16& sblk, float ref, bf16x8& pf0, bf16x8& pf1, float& sum) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(sblk[8 * half + e], scale_log2, -ref));
+            u32x4 w;
+            w.x = pack_bf16x2(p[0], p[1]);
+            w.y = pack_bf16x2(p[2], p[3]);
+            w.z = pack_bf16x2(p[4], p[5]);
+            w.w = pack_bf16x2(p[6], p[7]);
+            sum = dot2_sum(w.w, dot2_sum(w.z, dot2_sum(w.y, dot2_sum(w.x, sum))));
+            (half ? pf1 : pf0) = __builtin_bit_cast(bf16x8, w);
+        }
+    };
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    // Nothing may stay in flight into the loop: the loop's first MFMA reads the
-    // Q fragments, and a load still pending there would make every iteration
-    // wait for the next tile's prefetch as well.
+    f32x16 oacc[2][kDTiles];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t) oacc[nb][t] = f32x16{};
+    bf16x8 pprev[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) pprev[nb][s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    float ref[2] = {-INFINITY, -INFINITY};   // reference max, scaled base-2 units
+    float l[2] = {0.f, 0.f};                 // running sum over this lane's keys
+
     wait_all_memory();
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int j0 = kt * kBc;
-        lds_char* const kb = lds0 + (kt & 1) * (int)sizeof(Lds<D>);
-        lds_char* const vb = kb + kTileBytes;
-        if (kt + 1 < ntiles) load_tile(j0 + kBc);        // in flight during this tile
+    f32x16 scur[2][2];
+#pragma unroll
+    for (int t = 0; t < kDSteps; ++t) qk_step(k_s0, scur, t, t == 0);
 
-        // S^T = K . Q^T for keys j0 .. j0+63 (two independent 32-key chains).
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int t = 0; t < kDSteps; ++t) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const u32x4 w = *(lds_u32x4*)(kb + k_byte<D>(32 * u + n, 2 * t + hh));
-                sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[t],
-                                                                   sacc[u], 0, 0, 0);
-            }
+    // Operands of one 4-MFMA group of the pipelined step.  A score group
+    // (QK, d-step t) uses K rows n and 32+n and Q rows qrow0 and qrow0+32 of
+    // d-chunk 2t+hh; a P.V group uses the transposed V fragments of two d-tiles.
+    struct Ops {
+        u32x4 r[4];     // QK: a0, b0, a1, b1
+        s16x4 t[4];     // PV: lo/hi of d-tile 0, lo/hi of d-tile 1
+    };
+    auto issue_read = [&](const uint16_t* ks, const uint16_t* vs, int x, int gi, int r, Ops& op) {
+        if ((gi & 1) == 0) {
+            const int t = kStepsPerWindow * x + (gi >> 1);
+            const int chunk = 2 * t + hh;
+            lds_char* const base = (r & 1) ? (lds_char*)q_s : (lds_char*)ks;
+            const int row = ((r & 1) ? qrow0 : n) + ((r & 2) ? 32 : 0);
+            op.r[r] = *(lds_u32x4*)(base + k_byte<D>(row, chunk));
+        } else {
+            const int dt = 2 * (gi >> 1) + (r >> 1);
+            const int col = 32 * dt + vcol0;
+            const int row = 16 * x + vrow0 + ((r & 1) ? 8 : 0);
+            op.t[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((lds_char*)vs + v_byte<D>(row, col >> 3) + (col & 7) * 2));
         }
+    };
+    auto group_mfma = [&](int x, int gi, int m, const Ops& op, f32x16 (&sacc)[2][2]) {
+        if ((gi & 1) == 0) {
+            const int t = kStepsPerWindow * x + (gi >> 1);
+            const int nb = m >> 1, kb = m & 1;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, op.r[kb ? 2 : 0]);
+            const bf16x8 bq = __builtin_bit_cast(bf16x8, op.r[nb ? 3 : 1]);
+            const f32x16 z = {};
+            sacc[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, t == 0 ? z : sacc[nb][kb], 0, 0, 0);
+        } else {
+            const int dt = 2 * (gi >> 1) + (m >> 1), nb = m & 1;
+            const s16x4 lo = op.t[(m >> 1) * 2], hi = op.t[(m >> 1) * 2 + 1];
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            mfma_agpr(oacc[nb][dt], a, pprev[nb][x]);
+        }
+    };
 
-        // Mask (only tiles crossing the causal diagonal or the key end), tile max.
-        if ((j0 + kBc - 1) > wg_first_last) {
+    // One pipeline step for tile j (PAR = j % 3); tile t lives in k_s[t % 3]
+    // and v_s[t % 3].
+    auto step = [&](auto par_c, int j) {
+        constexpr int PAR = decltype(par_c)::value;
+        uint16_t* const ks[3] = {k_s0, k_s1, k_s2};
+        uint16_t* const vs[3] = {v_s0, v_s1, v_s2};
+        uint16_t* const k_fill = ks[(PAR + 2) % 3];        // <- tile j+2
+        uint16_t* const v_fill = vs[(PAR + 1) % 3];        // <- tile j+1
+        const uint16_t* const k_read = ks[(PAR + 1) % 3];  // tile j+1
+        const uint16_t* const v_read = vs[(PAR + 2) % 3];  // tile j-1
+
+        // The previous step's loads have landed, and every wavefront is done
+        // with the buffers refilled during this step.  The loads are issued
+        // from the main block below, also past the last tile (keys are
+        // clamped), which keeps that block free of branches.
+        wait_vmcnt<0>();
+        lds_barrier();
+
+        // The main block below is scheduled by hand, one slot at a time: an
+        // MFMA, the vector work of one or two softmax elements, and one LDS
+        // read of the next 4-MFMA group, fenced so the compiler keeps the
+        // order.  Groups alternate between a score step of tile j+1 (QK) and
+        // two d-tiles of the P.V product of tile j-1 (PV); the operands of a
+        // group are read during the group before it.
+        constexpr int kGroups = 2 * kStepsPerWindow;        // 4-MFMA groups per window
+        constexpr int kElems = 16 / (4 * kGroups);          // softmax elements per slot
+        // Operands are read kAhead groups ahead of their MFMAs.
+        constexpr int kAhead = 2;
+        Ops ops[kAhead + 1];
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+        for (int ga = 0; ga < kAhead; ++ga)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = j0 + 32 * u + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    if (key > my_last) sacc[u][j] = -INFINITY;
+            for (int r = 0; r < 4; ++r) issue_read(k_read, v_read, ga / kGroups, ga % kGroups, r, ops[ga]);
+
+        const int j0 = j * kBc;
+        if (j0 + kBc - 1 > wave_first_last) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+                        if (key > my_last[nb]) scur[nb][kb][e] = -INFINITY;
+                    }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Softmax element G (0..63) is element G%16 of block x = G/16, (nb, kb)
+        // = (x/2, x%2).  Its vector work runs as a pipeline over the slots so
+        // that no instruction waits on one issued in the same slot: slot i
+        // computes s*c - ref for the elements of slot i+2, their exponentials
+        // for slot i+1, packs slot i's values to bf16 and adds the packs of
+        // slot i-1 to the row sums.
+        f32x16 snext[2][2];
+        float psum[2] = {0.f, 0.f};
+        float xs[64], pe[64];
+        uint32_t pw[32];
+        constexpr int kSlots = 64 / kElems;
+        auto stage_a = [&](int sl) {
+#pragma unroll
+            for (int u = 0; u < kElems; ++u) {
+                const int G = sl * kElems + u;
+                if (sl < kSlots)
+                    xs[G] = fmaf(scur[G >> 5][(G >> 4) & 1][G & 15], scale_log2, -ref[G >> 5]);
+            }
+        };
+        auto stage_b = [&](int sl) {
+#pragma unroll
+            for (int u = 0; u < kElems; ++u) {
+                const int G = sl * kElems + u;
+                if (sl < kSlots) pe[G] = exp2_fast(xs[G]);
+            }
+        };
+        auto stage_c = [&](int sl) {
+#pragma unroll
+            for (int u = 0; u < kElems; ++u) {
+                const int G = sl * kElems + u;
+                if (sl >= 0 && sl < kSlots && (G & 1)) {
+                    pw[G >> 1] = pack_bf16x2(pe[G - 1], pe[G]);
+                    asm volatile("" ::"v"(pw[G >> 1]));   // keep the pack in its slot
                 }
-        }
-        float tmax = sacc[0][0];
+            }
+        };
+        float psum2[2] = {0.f, 0.f};
+        auto stage_d = [&](int sl) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < kElems; ++u) {
+                const int G = sl * kElems + u;
+                if (sl >= 0 && sl < kSlots) {
+                    if (G & 1) psum2[G >> 5] += pe[G];
+                    else psum[G >> 5] += pe[G];
+                }
+            }
+        };
+        stage_a(0);
+        stage_a(1);
+        stage_b(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[u][j]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
-        const bool raise = tmax > ref + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(raise)) {        // wave-uniform branch
-            const float ref_new = raise ? tmax : ref;
-            const float alpha = exp2_fast(ref - ref_new);  // 1 if kept, 0 on the first tile
-            ref = ref_new;
-            l *= alpha;
+        for (int x = 0; x < 4; ++x) {
 #pragma unroll
-            for (int t = 0; t < kDTiles; ++t) oacc[t] *= alpha;
-        }
-
-        // P = 2^(s*c - ref), bf16 B-operand fragments for the four 16-key steps:
-        // step s = 2u + half holds keys 16s + {4hh..4hh+3, 8+4hh..8+4hh+3}.
-        bf16x8 pf[4];
-        float psum4[4];
+            for (int gi = 0; gi < kGroups; ++gi) {
+                const int gg = x * kGroups + gi;
+                const Ops& cur = ops[gg % (kAhead + 1)];
+                Ops& nxt = ops[(gg + kAhead) % (kAhead + 1)];
+                const int nx = (gg + kAhead) / kGroups, ngi = (gg + kAhead) % kGroups;
+                // One wait per group: its four reads have landed (the next
+                // group's four may still be in flight).
+                if (gg + 1 < 4 * kGroups) wait_lgkmcnt<4>();
+                else wait_lgkmcnt<0>();
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(sacc[u][8 * half + e], scale_log2, -ref));
-                psum4[2 * u + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-                u32x4 w;
-                w.x = pack_bf16x2(p[0], p[1]);
-                w.y = pack_bf16x2(p[2], p[3]);
-                w.z = pack_bf16x2(p[4], p[5]);
-                w.w = pack_bf16x2(p[6], p[7]);
-                pf[2 * u + half] = __builtin_bit_cast(bf16x8, w);
+                for (int m = 0; m < 4; ++m) {
+                    const int sl = gg * 4 + m;
+                    group_mfma(x, gi, m, cur, snext);
+                    stage_a(sl + 2);
+                    stage_b(sl + 1);
+                    stage_c(sl);
+                    stage_d(sl - 1);
+                    if (gg + kAhead < 4 * kGroups) issue_read(k_read, v_read, nx, ngi, m, nxt);
+                    if ((sl & 3) == 1 && (sl >> 2) < 2 * kTileLoads) {
+                        const int li = sl >> 2;
+                        if (li < kTileLoads) issue_load(krsrc, st_kbase, k_fill, j + 2, li);
+                        else issue_load(vrsrc, st_vbase, v_fill, j + 1, li - kTileLoads);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
-        l += (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
+        stage_d(kSlots - 1);
+        psum[0] += psum2[0];
+        psum[1] += psum2[1];
+        bf16x8 pcur[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int w0 = 16 * nb + 4 * s4;
+                pcur[nb][s4] = __builtin_bit_cast(bf16x8, u32x4{pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]});
+            }
 
-        // O^T += V^T . P^T; the A operand of (t, s) is two transposed reads:
-        // keys 16s + 4hh + 0..3 and 16s + 8 + 4hh + 0..3 of column 32t + n.
+        // Rare: some p exceeded the bound (or this is the first tile).  Redo
+        // the tile against its true max and rescale what came before.
+        const bool over = !(psum[0] <= kSumLimit) || !(psum[1] <= kSumLimit);
+        if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+            for (int nb = 0; nb < 2; ++nb) {
+                float tm = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < kDTiles; ++t) {
-                const int col = 32 * t + vcol0;
-                const int row_a = 16 * s + vrow0;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(vb + v_byte<D>(row_a, col >> 3) + (col & 7) * 2));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(vb + v_byte<D>(row_a + 8, col >> 3) + (col & 7) * 2));
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], oacc[t], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) tm = fmaxf(tm, scur[nb][kb][e]);
+                tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+                const float rnew = fmaxf(ref[nb], tm * scale_log2);
+                const float alpha = rnew == ref[nb] ? 1.f : exp2_fast(ref[nb] - rnew);
+                const float ruse = rnew == -INFINITY ? 0.f : rnew;
+                ref[nb] = rnew;
+                l[nb] *= alpha;
+                if (nb == 0) agpr_settle(oacc);
+#pragma unroll
+                for (int t = 0; t < kDTiles; ++t) oacc[nb][t] *= alpha;
+                psum[nb] = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    softmax_block(scur[nb][kb], ruse, pcur[nb][2 * kb], pcur[nb][2 * kb + 1], psum[nb]);
             }
         }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            l[nb] += psum[nb];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) pprev[nb][s] = pcur[nb][s];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) scur[nb][kb] = snext[nb][kb];
+        }
+    };
 
-        if (kt + 1 < ntiles) store_tile((kt + 1) & 1);
-        __syncthreads();
+    for (int j = 0;;) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (++j >= ntiles) break;
+        step(std::integral_constant<int, 1>{}, j);
+        if (++j >= ntiles) break;
+        step(std::integral_constant<int, 2>{}, j);
+        if (++j >= ntiles) break;
     }
 
-    // Epilogue: combine the lane pair's partial sums, normalise, store bf16.
-    const float lt = l + __shfl_xor(l, 32, 64);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qlive) {
-        uint16_t* orow = o + qrow;
+    // P.V of the last tile.
+    wait_all_memory();
+    __syncthreads();
+    {
+        const int last = (ntiles - 1) % 3;
+        const uint16_t* const v_last = last == 0 ? v_s0 : (last == 1 ? v_s1 : v_s2);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) pv_step(v_last, oacc, pprev, s);
+    }
+
+    // Epilogue: combine the lane pair's partial sums, normalise, round to
+    // bf16, and write whole output rows.  Each lane holds 8-byte pieces of
+    // many rows, so the rows are first transposed through LDS: wavefront w
+    // owns one 16 KB K/V buffer (free now), stores its 64 rows x D as 8-byte
+    // units XOR-swizzled by row (unit u of row q at u ^ (q % units)), and
+    // reads them back as 16-byte row chunks, which it stores 4 rows per
+    // instruction.
+    agpr_settle(oacc);
+    float inv[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const float lt = l[nb] + __shfl_xor(l[nb], 32, 64);
+        inv[nb] = lt > 0.f ? 1.f / lt : 0.f;
+    }
+    constexpr int kUnits = D / 4;                           // 8-byte units per row
+    __syncthreads();                                        // every wave is done with the K/V tiles
+    uint16_t* const obuf_w[4] = {k_s0, k_s1, k_s2, v_s0};
+    lds_char* const obuf = (lds_char*)(wave_u == 0 ? obuf_w[0] : wave_u == 1 ? obuf_w[1]
+                                       : wave_u == 2 ? obuf_w[2] : obuf_w[3]);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int q = 32 * nb + n;
 #pragma unroll
         for (int t = 0; t < kDTiles; ++t) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-                const int d0 = 32 * t + 8 * grp + 4 * hh;
+                const int u = (32 * t + 8 * grp + 4 * hh) / 4;
                 u32x2 w;
-                w.x = pack_bf16x2(oacc[t][4 * grp + 0] * inv, oacc[t][4 * grp + 1] * inv);
-                w.y = pack_bf16x2(oacc[t][4 * grp + 2] * inv, oacc[t][4 * grp + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + d0) = w;
+                w.x = pack_bf16x2(oacc[nb][t][4 * grp + 0] * inv[nb], oacc[nb][t][4 * grp + 1] * inv[nb]);
+                w.y = pack_bf16x2(oacc[nb][t][4 * grp + 2] * inv[nb], oacc[nb][t][4 * grp + 3] * inv[nb]);
+                *(__attribute__((address_space(3))) u32x2*)(obuf + q * D * 2 + 8 * (u ^ (q & (kUnits - 1)))) = w;
             }
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < kChunks; ++x) {
+        const int sidx = 64 * x + lane;
+        const int q = sidx / kChunks, m = sidx % kChunks;
+        const int sw = q & (kUnits - 1);
+        u32x4 w = *(lds_u32x4*)(obuf + q * D * 2 + 16 * (m ^ (sw >> 1)));
+        if (sw & 1) w = u32x4{w.z, w.w, w.x, w.y};
+        const int r = 64 * wave + q;
+        const int pos = p0 + (r >> lg);
+        if (pos < Sq) {
+            const int head = hk * g + (r & (g - 1));
+            uint16_t* const dst = o + (((size_t)b * Hq + head) * Sq + pos) * D + 8 * m;
+            *reinterpret_cast<u32x4*>(dst) = w;
         }
     }
 }
@@ -298,8 +637,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int g = a.Hq / a.Hkv;
     int lg = 0;
     while ((1 << lg) < g) ++lg;
-    const int P = kRowsWG >> lg;
-    const int nqb = (a.Sq + P - 1) / P;
+    const int npos = kRowsWG >> lg;
+    const int nqb = (a.Sq + npos - 1) / npos;
     dim3 grid(nqb * a.Hkv * a.B);
     const float sl = a.scale * kLog2e;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
