@@ -92,7 +92,7 @@ def build(verbose: bool = False) -> str:
     except ImportError:          # run as a script: this directory is on sys.path
         import asm_check
     for out, _ in asm_jobs:
-        problems = asm_check.check(open(out).read())
+        problems = asm_check.check_all(open(out).read())
         if problems:
             raise RuntimeError(f"MFMA wait-state check failed for {out}:\n" + "\n".join(problems))
     if verbose:

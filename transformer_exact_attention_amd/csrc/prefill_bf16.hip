@@ -14,10 +14,11 @@
 //   * wavefront w owns rows 64w..64w+63 as two 32-row blocks nb = 0, 1; lane i
 //     owns query column i%32 of each block and lane half hh = i/32 (the MFMA
 //     operand split along the contraction);
-//   * the Q rows are staged in LDS once; K/V tiles of 64 keys are staged in
-//     LDS by direct-to-LDS buffer loads, three buffers each (Q and the six
-//     tiles fill the 160 KB LDS), and serve all 256 rows: the g query heads
-//     of a group share them.  The step that computes the scores of tile j+1
+//   * each wavefront reads its Q fragments from global memory once and keeps
+//     them in AGPRs, where the score MFMAs take them as B operand; K/V tiles
+//     of 64 keys are staged in LDS by direct-to-LDS buffer loads, three
+//     buffers each, and serve all 256 rows: the g query heads of a group
+//     share them.  The step that computes the scores of tile j+1
 //     loads K tile j+2 and V tile j+1, spread over its first half so that the
 //     four wavefronts do not queue 32 KB of requests at once.
 //
@@ -94,6 +95,16 @@ __device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Score MFMAs: the Q^T operand comes from AGPRs (it is read from global
+// memory once and never changes), the accumulator stays in VGPRs for the
+// softmax.  The same wait-state caveat as mfma_agpr applies.
+__device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& k, const bf16x8& q) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& k, const bf16x8& q) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+}
+
 // Workgroup barrier without a memory fence.  Every wavefront first waits for
 // its own direct-to-LDS loads whose data the others are about to read; a
 // fenced barrier would also wait for the loads still meant to be in flight.
@@ -146,12 +157,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     constexpr int kDSteps = D / 16;                         // MFMA contraction steps over d
     constexpr int kDTiles = D / 32;                         // 32-row output tiles of O^T
     constexpr int kTileLoads = kBc * kChunks / 64 / kWaves; // 1 KB direct loads per wavefront per tile
-    constexpr int kQLoads = kRowsWG * kChunks / 64 / kWaves;
     constexpr int kStepsPerWindow = kDSteps / 4;            // score steps per pipeline window
 
     // Separate arrays, so that the compiler can tell the buffers being filled
     // by direct loads from the ones being read.
-    __shared__ __attribute__((aligned(1024))) uint16_t q_s[kRowsWG * D];
     __shared__ __attribute__((aligned(1024))) uint16_t k_s0[kBc * D];
     __shared__ __attribute__((aligned(1024))) uint16_t k_s1[kBc * D];
     __shared__ __attribute__((aligned(1024))) uint16_t k_s2[kBc * D];
@@ -221,39 +230,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         st_kbase = (uint32_t)(row * D * 2 + 16 * (pp ^ k_swz<D>(row)));
         st_vbase = (uint32_t)(row * D * 2 + 16 * (pp ^ v_swz<D>(row)));
     }
-    auto issue_load = [&](__amdgpu_buffer_rsrc_t r, uint32_t vbase, uint16_t* dst, int tile, int x) {
+    // wave_lds = 1024 * wave; passing it through an empty asm once per step
+    // keeps the compiler from precomputing every load's LDS address in its
+    // own scalar register (they would not fit and get spilled).
+    auto issue_load = [&](__amdgpu_buffer_rsrc_t r, uint32_t vbase, uint16_t* dst, int tile, int x, int wave_lds) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (lds_void*)((lds_char*)(dst) + 1024 * (4 * x + wave_u)), 16,
+            r, (lds_void*)((lds_char*)(dst) + 4096 * x + wave_lds), 16,
             vbase + (uint32_t)(tile * (kBc * D * 2) + 4096 * x), 0, 0, 0);
     };
     auto issue_tile = [&](__amdgpu_buffer_rsrc_t r, uint32_t vbase, uint16_t* dst, int tile) {
 #pragma unroll
-        for (int x = 0; x < kTileLoads; ++x) issue_load(r, vbase, dst, tile, x);
+        for (int x = 0; x < kTileLoads; ++x) issue_load(r, vbase, dst, tile, x, 1024 * wave_u);
     };
 
-    // Q rows of the workgroup -> LDS, once, through registers (16-byte
-    // chunks, same swizzle as K).  Ordinary loads keep the compiler's
-    // tracking of direct-to-LDS targets to the K/V buffers of the loop.
-    {
-        const uint16_t* qgroup = q + ((size_t)b * Hq + (size_t)hk * g) * (size_t)Sq * D;
-        constexpr int kBatch = kQLoads;
+    // Q^T operand fragments of this lane's two query columns: Q[row][16t +
+    // 8hh .. +8] for d-step t (rows past Sq read the last row; never stored).
+    bf16x8 qa[2][kDSteps];
 #pragma unroll
-        for (int x0 = 0; x0 < kQLoads; x0 += kBatch) {
-            u32x4 qv[kBatch];
+    for (int nb = 0; nb < 2; ++nb) {
+        const int r = 64 * wave + 32 * nb + n;
+        const int pos = min(p0 + (r >> lg), Sq - 1);
+        const uint16_t* const qrow = q + (((size_t)b * Hq + hk * g + (r & (g - 1))) * Sq + pos) * D + 8 * hh;
 #pragma unroll
-            for (int x = 0; x < kBatch; ++x) {
-                const int row = (tid + kThreads * (x0 + x)) / kChunks;
-                const int c = (tid + kThreads * (x0 + x)) % kChunks;
-                const int prow = min(p0 + (row >> lg), Sq - 1);
-                qv[x] = *reinterpret_cast<const u32x4*>(qgroup + ((size_t)(row & (g - 1)) * Sq + prow) * D + 8 * c);
-            }
-#pragma unroll
-            for (int x = 0; x < kBatch; ++x) {
-                const int row = (tid + kThreads * (x0 + x)) / kChunks;
-                const int c = (tid + kThreads * (x0 + x)) % kChunks;
-                *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(row, c)) = qv[x];
-            }
-        }
+        for (int t = 0; t < kDSteps; ++t) qa[nb][t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t);
     }
     // Zero the K/V tiles (the first step also multiplies a zero P by V
     // buffer 2), then start K tiles 0, 1 and V tile 0.
@@ -272,20 +271,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     issue_tile(vrsrc, st_vbase, v_s0, 0);
 
     // ---- operand reads -------------------------------------------------
-    const int qrow0 = 64 * wave + n;
+    auto qk_mfma = [&](f32x16& acc, const u32x4& kfrag, const bf16x8& qf, bool first) {
+        if (first) mfma_qk_first(acc, __builtin_bit_cast(bf16x8, kfrag), qf);
+        else mfma_qk(acc, __builtin_bit_cast(bf16x8, kfrag), qf);
+    };
     auto qk_step = [&](const uint16_t* ks, f32x16 (&sacc)[2][2], int t, bool first) {
         const u32x4 a0 = *(lds_u32x4*)((lds_char*)ks + k_byte<D>(n, 2 * t + hh));
         const u32x4 a1 = *(lds_u32x4*)((lds_char*)ks + k_byte<D>(32 + n, 2 * t + hh));
-        const u32x4 b0 = *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(qrow0, 2 * t + hh));
-        const u32x4 b1 = *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(qrow0 + 32, 2 * t + hh));
-        const f32x16 z = {};
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            const bf16x8 bq = __builtin_bit_cast(bf16x8, nb ? b1 : b0);
-            sacc[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), bq,
-                                                                  first ? z : sacc[nb][0], 0, 0, 0);
-            sacc[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), bq,
-                                                                  first ? z : sacc[nb][1], 0, 0, 0);
+            qk_mfma(sacc[nb][0], a0, qa[nb][t], first);
+            qk_mfma(sacc[nb][1], a1, qa[nb][t], first);
         }
     };
     // Transposed V reads: in 16-lane group G = lane/16, lane rr = lane%16 points
@@ -347,19 +343,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     for (int t = 0; t < kDSteps; ++t) qk_step(k_s0, scur, t, t == 0);
 
     // Operands of one 4-MFMA group of the pipelined step.  A score group
-    // (QK, d-step t) uses K rows n and 32+n and Q rows qrow0 and qrow0+32 of
-    // d-chunk 2t+hh; a P.V group uses the transposed V fragments of two d-tiles.
+    // (QK, d-step t) reads K rows n and 32+n of d-chunk 2t+hh (two LDS
+    // reads); a P.V group reads the transposed V fragments of two d-tiles
+    // (four LDS reads).
     struct Ops {
-        u32x4 r[4];     // QK: a0, b0, a1, b1
+        u32x4 r[2];     // QK: K rows n, 32+n
         s16x4 t[4];     // PV: lo/hi of d-tile 0, lo/hi of d-tile 1
     };
+    auto group_reads = [](int gi) { return (gi & 1) == 0 ? 2 : 4; };
     auto issue_read = [&](const uint16_t* ks, const uint16_t* vs, int x, int gi, int r, Ops& op) {
         if ((gi & 1) == 0) {
             const int t = kStepsPerWindow * x + (gi >> 1);
-            const int chunk = 2 * t + hh;
-            lds_char* const base = (r & 1) ? (lds_char*)q_s : (lds_char*)ks;
-            const int row = ((r & 1) ? qrow0 : n) + ((r & 2) ? 32 : 0);
-            op.r[r] = *(lds_u32x4*)(base + k_byte<D>(row, chunk));
+            op.r[r] = *(lds_u32x4*)((lds_char*)ks + k_byte<D>(n + 32 * r, 2 * t + hh));
         } else {
             const int dt = 2 * (gi >> 1) + (r >> 1);
             const int col = 32 * dt + vcol0;
@@ -372,10 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         if ((gi & 1) == 0) {
             const int t = kStepsPerWindow * x + (gi >> 1);
             const int nb = m >> 1, kb = m & 1;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, op.r[kb ? 2 : 0]);
-            const bf16x8 bq = __builtin_bit_cast(bf16x8, op.r[nb ? 3 : 1]);
-            const f32x16 z = {};
-            sacc[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, t == 0 ? z : sacc[nb][kb], 0, 0, 0);
+            qk_mfma(sacc[nb][kb], op.r[kb], qa[nb][t], t == 0);
         } else {
             const int dt = 2 * (gi >> 1) + (m >> 1), nb = m & 1;
             const s16x4 lo = op.t[(m >> 1) * 2], hi = op.t[(m >> 1) * 2 + 1];
@@ -401,6 +393,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         // clamped), which keeps that block free of branches.
         wait_vmcnt<0>();
         lds_barrier();
+        int wave_lds = 1024 * wave_u;
+        asm volatile("" : "+s"(wave_lds));
 
         // The main block below is scheduled by hand, one slot at a time: an
         // MFMA, the vector work of one or two softmax elements, and one LDS
@@ -416,7 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int ga = 0; ga < kAhead; ++ga)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) issue_read(k_read, v_read, ga / kGroups, ga % kGroups, r, ops[ga]);
+            for (int r = 0; r < group_reads(ga % kGroups); ++r)
+                issue_read(k_read, v_read, ga / kGroups, ga % kGroups, r, ops[ga]);
 
         const int j0 = j * kBc;
         if (j0 + kBc - 1 > wave_first_last) {
@@ -491,10 +486,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 const Ops& cur = ops[gg % (kAhead + 1)];
                 Ops& nxt = ops[(gg + kAhead) % (kAhead + 1)];
                 const int nx = (gg + kAhead) / kGroups, ngi = (gg + kAhead) % kGroups;
-                // One wait per group: its four reads have landed (the next
-                // group's four may still be in flight).
-                if (gg + 1 < 4 * kGroups) wait_lgkmcnt<4>();
-                else wait_lgkmcnt<0>();
+                // One wait per group: its reads have landed (the next
+                // group's may still be in flight).
+                if (gg + 1 >= 4 * kGroups) wait_lgkmcnt<0>();
+                else if (group_reads((gg + 1) % kGroups) == 4) wait_lgkmcnt<4>();
+                else wait_lgkmcnt<2>();
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int sl = gg * 4 + m;
@@ -503,11 +499,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                     stage_b(sl + 1);
                     stage_c(sl);
                     stage_d(sl - 1);
-                    if (gg + kAhead < 4 * kGroups) issue_read(k_read, v_read, nx, ngi, m, nxt);
+                    if (gg + kAhead < 4 * kGroups && m < group_reads(ngi))
+                        issue_read(k_read, v_read, nx, ngi, m, nxt);
                     if ((sl & 3) == 1 && (sl >> 2) < 2 * kTileLoads) {
                         const int li = sl >> 2;
-                        if (li < kTileLoads) issue_load(krsrc, st_kbase, k_fill, j + 2, li);
-                        else issue_load(vrsrc, st_vbase, v_fill, j + 1, li - kTileLoads);
+                        if (li < kTileLoads) issue_load(krsrc, st_kbase, k_fill, j + 2, li, wave_lds);
+                        else issue_load(vrsrc, st_vbase, v_fill, j + 1, li - kTileLoads, wave_lds);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
