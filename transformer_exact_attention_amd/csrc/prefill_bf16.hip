@@ -167,6 +167,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t v_s0[kBc * D];
     __shared__ __attribute__((aligned(1024))) uint16_t v_s1[kBc * D];
     __shared__ __attribute__((aligned(1024))) uint16_t v_s2[kBc * D];
+    // Q rows of the workgroup (read into registers once), then the output
+    // transpose of the epilogue.
+    __shared__ __attribute__((aligned(1024))) uint16_t q_s[kRowsWG * D];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -243,17 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         for (int x = 0; x < kTileLoads; ++x) issue_load(r, vbase, dst, tile, x, 1024 * wave_u);
     };
 
-    // Q^T operand fragments of this lane's two query columns: Q[row][16t +
-    // 8hh .. +8] for d-step t (rows past Sq read the last row; never stored).
-    bf16x8 qa[2][kDSteps];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int r = 64 * wave + 32 * nb + n;
-        const int pos = min(p0 + (r >> lg), Sq - 1);
-        const uint16_t* const qrow = q + (((size_t)b * Hq + hk * g + (r & (g - 1))) * Sq + pos) * D + 8 * hh;
-#pragma unroll
-        for (int t = 0; t < kDSteps; ++t) qa[nb][t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t);
-    }
+    bf16x8 qa[2][kDSteps];   // filled from q_s once the loads have landed
     // Zero the K/V tiles (the first step also multiplies a zero P by V
     // buffer 2), then start K tiles 0, 1 and V tile 0.
     for (int i = tid; i < kBc * D / 8; i += kThreads) {
@@ -266,6 +259,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         ((lds_u32x4*)(lds_char*)v_s2)[i] = z;
     }
     __syncthreads();
+    // Q rows of the workgroup -> LDS by direct loads (16 lanes per row, so
+    // whole rows are fetched), swizzled like K; rows past Sq read the last
+    // row and are never stored.
+    {
+        constexpr int kQLoads = kRowsWG * kChunks / 64 / kWaves;
+        const uint16_t* qgroup = q + ((size_t)b * Hq + (size_t)hk * g) * (size_t)Sq * D;
+#pragma unroll
+        for (int x = 0; x < kQLoads; ++x) {
+            const int t = wave * kQLoads + x;
+            const int s = 64 * t + lane;
+            const int row = s / kChunks, pp = s % kChunks;
+            const int c = pp ^ k_swz<D>(row);
+            const int prow = min(p0 + (row >> lg), Sq - 1);
+            const uint16_t* src = qgroup + ((size_t)(row & (g - 1)) * Sq + prow) * D + 8 * c;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (lds_void*)((lds_char*)q_s + 1024 * t), 16, 0, 0);
+        }
+    }
     issue_tile(krsrc, st_kbase, k_s0, 0);
     issue_tile(krsrc, st_kbase, k_s1, 1);
     issue_tile(vrsrc, st_vbase, v_s0, 0);
@@ -338,6 +349,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     wait_all_memory();
     __syncthreads();
+    // Q^T operand fragments of this lane's two query columns: Q[row][16t +
+    // 8hh .. +8] for d-step t, kept in AGPRs.
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int t = 0; t < kDSteps; ++t)
+            qa[nb][t] = __builtin_bit_cast(
+                bf16x8, *(lds_u32x4*)((lds_char*)q_s + k_byte<D>(64 * wave + 32 * nb + n, 2 * t + hh)));
     f32x16 scur[2][2];
 #pragma unroll
     for (int t = 0; t < kDSteps; ++t) qk_step(k_s0, scur, t, t == 0);
@@ -580,10 +599,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // Epilogue: combine the lane pair's partial sums, normalise, round to
     // bf16, and write whole output rows.  Each lane holds 8-byte pieces of
     // many rows, so the rows are first transposed through LDS: wavefront w
-    // owns one 16 KB K/V buffer (free now), stores its 64 rows x D as 8-byte
-    // units XOR-swizzled by row (unit u of row q at u ^ (q % units)), and
-    // reads them back as 16-byte row chunks, which it stores 4 rows per
-    // instruction.
+    // stores its 64 rows x D in its quarter of the Q area (free since the
+    // prologue) as 8-byte units XOR-swizzled by row (unit u of row q at
+    // u ^ (q % units)), and reads them back as 16-byte row chunks, which it
+    // stores 4 rows per instruction.
     agpr_settle(oacc);
     float inv[2];
 #pragma unroll
@@ -592,10 +611,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         inv[nb] = lt > 0.f ? 1.f / lt : 0.f;
     }
     constexpr int kUnits = D / 4;                           // 8-byte units per row
-    __syncthreads();                                        // every wave is done with the K/V tiles
-    uint16_t* const obuf_w[4] = {k_s0, k_s1, k_s2, v_s0};
-    lds_char* const obuf = (lds_char*)(wave_u == 0 ? obuf_w[0] : wave_u == 1 ? obuf_w[1]
-                                       : wave_u == 2 ? obuf_w[2] : obuf_w[3]);
+    lds_char* const obuf = (lds_char*)q_s + wave_u * (64 * D * 2);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int q = 32 * nb + n;
