@@ -60,7 +60,6 @@ def kernel_traffic(name: str, source_files):
     WRITE_SIZE, scaled by a plain copy's counters) and returns its bytes only
     if the recorded source digest matches the kernel sources today.
     """
-    import hashlib
     path = os.path.join(PROFILES, f"{name}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -69,12 +68,22 @@ def kernel_traffic(name: str, source_files):
     t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
     if not m or not t:
         return None
-    h = hashlib.sha256()
-    for f in source_files:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != m.group(1):
+    if source_digest(open(os.path.join(ROOT, f)).read() for f in source_files) != m.group(1):
         return None
     return float(t.group(1))
+
+
+def source_digest(texts) -> str:
+    """sha256 over the code of kernel sources, comments and blank lines removed
+    (so that documentation edits do not retire measured counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    for text in texts:
+        for line in text.splitlines():
+            code = re.sub(r"\s*//.*$", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 def cpu_baseline_prefill(w, q, k, v, budget_s=12.0):

@@ -14,8 +14,10 @@
 //   * wavefront w owns rows 64w..64w+63 as two 32-row blocks nb = 0, 1; lane i
 //     owns query column i%32 of each block and lane half hh = i/32 (the MFMA
 //     operand split along the contraction);
-//   * each wavefront reads its Q fragments from global memory once and keeps
-//     them in AGPRs, where the score MFMAs take them as B operand; K/V tiles
+//   * the workgroup's Q rows are staged once through LDS (whole-row loads);
+//     each wavefront then keeps its Q fragments in AGPRs, where the score
+//     MFMAs take them as B operand, and the Q area is reused at the end to
+//     transpose the output for row-contiguous stores; K/V tiles
 //     of 64 keys are staged in LDS by direct-to-LDS buffer loads, three
 //     buffers each, and serve all 256 rows: the g query heads of a group
 //     share them.  The step that computes the scores of tile j+1
@@ -46,8 +48,8 @@
 // accumulator and sum rescaled) only when some lane's tile sum of p exceeds
 // 2^8, which bounds every p by 2^8.  Softmax does not depend on the reference
 // point, so the result is exact up to rounding.  P is rounded to bf16 for the
-// PV product and the row sums add exactly those rounded values (v_dot2 with
-// fp32 accumulation); accumulation is fp32 throughout.
+// PV product; the row sums add the fp32 values of p (the recomputing path adds
+// the rounded ones); accumulation is fp32 throughout.
 #include "common.hpp"
 #include "launch.hpp"
 
