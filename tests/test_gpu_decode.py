@@ -83,6 +83,22 @@ def test_decode_peaked(ga):
     assert_close(to_f64(o), ref, "bf16", "decode peaked", beyond_unit=True)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 1)])
+def test_decode_rising_scores_force_rescales(ga, Hq, Hkv):
+    # key norms grow with the token index, so the running max of every piece
+    # keeps rising and the lazily rescaled accumulators are redone many times
+    lens = np.array([1500, 2048, 5, 600], np.int32)
+    q = W.normal([43, 0], (4, Hq, 128), "f32")
+    kc = W.normal([43, 1], (4, Hkv, 2048, 128), "f32") * (1 + np.arange(2048, dtype=np.float32) / 100)[:, None]
+    kc[:, :, 1333] *= 3
+    vc = W.normal([43, 2], (4, Hkv, 2048, 128), "f32")
+    q, kc, vc = (W.f32_to_bf16_bits(x) for x in (q, kc, vc))
+    note(f"decode rising scores Hq{Hq} Hkv{Hkv}")
+    o = run_contig(ga, q, kc, vc, lens)
+    ref = oracle.decode_contiguous(ref_f64(q, "bf16"), ref_f64(kc, "bf16"), ref_f64(vc, "bf16"), lens)
+    assert_close(to_f64(o), ref, "bf16", "decode rising scores", beyond_unit=True)
+
+
 def test_paged_equals_contiguous_bitwise_and_permutation_invariant(ga):
     import torch
     B, Hq, Hkv = 6, 32, 8

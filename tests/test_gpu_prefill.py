@@ -88,6 +88,22 @@ def test_bf16_peaked_softmax(ga, qmul):
     check_vs_oracle(ga, q, k, v, "bf16", True, None, f"peaked x{qmul}", beyond_unit=True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_rising_scores_force_rescales(ga, d, causal):
+    # Key norms grow along the sequence and one late key dominates from inside a
+    # tile, so every row's running max rises tile after tile: the kernel has to
+    # recompute tiles against a new maximum and rescale the partial output and
+    # sum many times per row.
+    B, Hq, Hkv, S = 1, 8, 2, 700
+    q = W.normal([23, 0], (B, Hq, S, d), "f32")
+    k = W.normal([23, 1], (B, Hkv, S, d), "f32") * (1 + np.arange(S, dtype=np.float32) / 50)[:, None]
+    k[:, :, 451] *= 4
+    v = W.normal([23, 2], (B, Hkv, S, d), "f32")
+    q, k, v = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+    check_vs_oracle(ga, q, k, v, "bf16", causal, None, "rising scores", beyond_unit=True)
+
+
 def test_bf16_explicit_scale(ga):
     q, k, v = inputs(15, 1, 4, 2, 96, 160, 128, "bf16")
     check_vs_oracle(ga, q, k, v, "bf16", True, 0.37, "scale 0.37")
