@@ -49,6 +49,14 @@ constexpr int kChunk = 32;               // tokens per pipeline stage (two 16-to
 constexpr float kRescaleSlack = 8.0f;    // base-2 units, as in the prefill kernel
 constexpr int kStreamAux = 2;            // non-temporal loads: every K/V byte is read once
 
+// A 64-bit value the compiler cannot prove wavefront-uniform (it came from
+// LDS) made uniform explicitly, so what derives from it stays scalar.
+__device__ __forceinline__ long long uniform64(long long x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // Q tokens per wavefront share: W / NW rounded up to 16, at least kDecodeMinShare.
 __device__ __forceinline__ long long share_tokens(long long W, long long NW) {
     long long q = (W + NW - 1) / NW;
@@ -119,10 +127,10 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
             for (int i = tid; i <= B; i += kThreads) prefix_out[i] = pre[i];
     }
 
-    const long long W = pre[B] * Hkv;
+    const long long W = uniform64(pre[B] * Hkv);
     const long long NW = (long long)gridDim.x * kWaves;
     const long long Q = share_tokens(W, NW);
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c = lane & 15;
     const int q4 = lane >> 4;
@@ -131,182 +139,192 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     const long long end = min(start + Q, W);
 
     typedef u32x4 Buf[2][4];
+    if (start >= end) return;
 
-    for (long long pos = start; pos < end;) {
-        // Segment (b, hk) holding flattened position pos: largest b with pre[b]*Hkv <= pos.
+    // A piece: the part of one segment (b, hk) inside this wavefront's share,
+    // tokens [p0, p1) of the segment, streamed as 32-token chunks from the
+    // 16-aligned token c0.  Everything in it is wavefront-uniform
+    // (readfirstlane makes that explicit, so table lookups are scalar loads).
+    struct Piece {
+        int b, hk, p0, p1, slot, c0, nchunks;
+        long long next;                     // flattened position after the piece
+    };
+    auto describe = [&](long long pos) {
+        // segment holding pos: largest b with pre[b]*Hkv <= pos
         int lo = 0, hi = B - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (pre[mid] * Hkv <= pos) lo = mid; else hi = mid - 1;
         }
-        // Everything describing the piece is wavefront-uniform; readfirstlane
-        // makes that explicit, so table lookups become scalar loads.
-        const int b = __builtin_amdgcn_readfirstlane(lo);
-        const int L = __builtin_amdgcn_readfirstlane((int)(pre[b + 1] - pre[b]));
-        const long long seg0 = pre[b] * Hkv;
-        const int hk = __builtin_amdgcn_readfirstlane((int)((pos - seg0) / L));
-        const long long S = seg0 + (long long)hk * L;                 // segment start
-        const int p0 = __builtin_amdgcn_readfirstlane((int)(pos - S));
-        const int p1 = __builtin_amdgcn_readfirstlane((int)(min(end, S + L) - S));   // piece: tokens [p0, p1)
-        const int slot = __builtin_amdgcn_readfirstlane((int)(w - S / Q));          // partial index in the segment
-        pos = S + p1;
+        Piece p;
+        p.b = __builtin_amdgcn_readfirstlane(lo);
+        const int L = __builtin_amdgcn_readfirstlane((int)(pre[p.b + 1] - pre[p.b]));
+        const long long seg0 = uniform64(pre[p.b] * Hkv);
+        p.hk = __builtin_amdgcn_readfirstlane((int)((pos - seg0) / L));
+        const long long S = seg0 + (long long)p.hk * L;               // segment start
+        p.p0 = __builtin_amdgcn_readfirstlane((int)(pos - S));
+        p.p1 = __builtin_amdgcn_readfirstlane((int)(min(end, S + L) - S));
+        p.slot = __builtin_amdgcn_readfirstlane((int)(w - S / Q));  // partial index in the segment
+        p.c0 = p.p0 & ~15;
+        p.nchunks = (p.p1 - p.c0 + kChunk - 1) / kChunk;            // >= 1
+        p.next = S + p.p1;
+        return p;
+    };
+    const Piece none = {0, 0, 0, 0, 0, 0, 0, end};                  // loads nothing
 
-        // Q^T operand: lane holds Q[head hb*16 + c][32*ds + 8*q4 .. +8] (zero for heads >= g).
-        bf16x8 qf[NHB][4];
+    // Q^T operand: lane holds Q[head hb*16 + c][32*ds + 8*q4 .. +8].  Columns
+    // of heads >= g repeat the group's first head (their results are never
+    // written; every column of the MFMAs is independent), so the loads need
+    // no branch.
+    auto load_q = [&](bf16x8 (&qf)[NHB][4], const Piece& p) {
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             const int hl = hb * 16 + c;
-            const bool hv = hl < g;
-            const uint16_t* qp = q + ((size_t)b * Hq + hk * g + (hv ? hl : 0)) * kD;
+            const uint16_t* qp = q + ((size_t)p.b * Hq + p.hk * g + (hl < g ? hl : 0)) * kD;
 #pragma unroll
-            for (int ds = 0; ds < 4; ++ds) {
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (hv) x = *reinterpret_cast<const u32x4*>(qp + 32 * ds + 8 * q4);
-                qf[hb][ds] = __builtin_bit_cast(bf16x8, x);
-            }
+            for (int ds = 0; ds < 4; ++ds)
+                qf[hb][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * ds + 8 * q4));
         }
+    };
 
-        float ref[NHB], lsum[NHB];
-        f32x4 oacc[NHB][8];
+    // Chunk x of the stream seen from piece cur, whose chunks are processed in
+    // pairs: with ne = nchunks rounded up to even, x < nchunks is cur's own
+    // chunk, nchunks <= x < ne an empty slot, x == ne the next piece's chunk 0
+    // (prefetched while cur finishes) and x == ne + 1 the next piece's chunk 1
+    // (table entries only).  A piece therefore always starts with its chunk 0
+    // in buffer A.
+    struct Src {
+        int b, hk, c0, p1, ci;
+    };
+    auto src_of = [&](const Piece& cur, const Piece& nxt, int x) {
+        const int ne = (cur.nchunks + 1) & ~1;
+        const bool own = x < cur.nchunks;
+        Src r;
+        r.b = own ? cur.b : nxt.b;
+        r.hk = own ? cur.hk : nxt.hk;
+        r.c0 = own ? cur.c0 : nxt.c0;
+        r.p1 = own ? cur.p1 : (x >= ne ? nxt.p1 : 0);
+        r.ci = own ? x : (x >= ne ? x - ne : 0);      // empty slot: token 0, nothing valid
+        return r;
+    };
+    // Table entries of a chunk's two blocks, fetched one chunk ahead of the
+    // loads that use them.
+    auto lookup = [&](int (&ph)[2], const Src& sr) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int t0 = sr.c0 + sr.ci * kChunk + 16 * blk;
+            ph[blk] = t0 < sr.p1 ? rows.lookup(table, sr.b, t0 >> 4) : 0;
+        }
+    };
+    // Every load is issued unconditionally through a buffer resource that
+    // covers only the block's tokens below p1: the hardware returns zeros
+    // beyond it (chunks past the end cost no memory traffic).  With a fixed
+    // number of loads per chunk the wait counts stay exact, so the next
+    // chunk streams in while the current one is computed.
+    auto load = [&](Buf& kr, Buf& vr, const int (&ph)[2], const Src& sr) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int t0 = sr.c0 + sr.ci * kChunk + 16 * blk;
+            // (uniform; kept in scalar registers so the descriptors are too)
+            const int nvalid = __builtin_amdgcn_readfirstlane(min(max(sr.p1 - t0, 0), 16));
+            const size_t off = nvalid > 0 ? rows.offset(ph[blk], sr.b, sr.hk, t0) : 0;
+            const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows.kbase + off, (uint32_t)nvalid * kD * 2);
+            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows.vbase + off, (uint32_t)nvalid * kD * 2);
+#pragma unroll
+            for (int ds = 0; ds < 4; ++ds)
+                kr[blk][ds] = __builtin_amdgcn_raw_buffer_load_b128(
+                    krs, (uint32_t)(c * kD + 32 * ds + 8 * q4) * 2, 0, kStreamAux);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                vr[blk][rr] = __builtin_amdgcn_raw_buffer_load_b128(
+                    vrs, (uint32_t)((4 * q4 + rr) * kD + 8 * c) * 2, 0, kStreamAux);
+        }
+    };
+
+    bf16x8 qf[NHB][4], qn[NHB][4];
+    float ref[NHB], lsum[NHB];
+    f32x4 oacc[NHB][8];
+
+    auto process = [&](const Buf& kr, const Buf& vr, const Piece& cur, int ci) {
+        bf16x4 pf[NHB][2];
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
-            ref[hb] = -INFINITY;
-            lsum[hb] = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) oacc[hb][j] = f32x4{};
-        }
-
-        const int c0 = p0 & ~15;                                   // first 16-aligned block
-        const int nchunks = (p1 - c0 + kChunk - 1) / kChunk;       // >= 1
-
-        // Table entries of a chunk's two blocks (wavefront-uniform scalar loads),
-        // fetched one chunk ahead of the loads that use them.
-        auto lookup = [&](int (&ph)[2], int ci) {
+            float s[2][4];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
-                const int t0 = c0 + ci * kChunk + 16 * blk;
-                ph[blk] = t0 < p1 ? rows.lookup(table, b, t0 >> 4) : 0;
-            }
-        };
-        // Every load is issued unconditionally through a buffer resource that
-        // covers only the block's tokens below p1: the hardware returns zeros
-        // beyond it (chunks past the end cost no memory traffic).  With a fixed
-        // number of loads per chunk the wait counts stay exact, so chunk i+1
-        // streams in while chunk i is computed.
-        auto load = [&](Buf& kr, Buf& vr, const int (&ph)[2], int ci) {
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int t0 = c0 + ci * kChunk + 16 * blk;
-                // (uniform; kept in scalar registers so the descriptors are too)
-                const int nvalid = __builtin_amdgcn_readfirstlane(min(max(p1 - t0, 0), 16));
-                const size_t off = nvalid > 0 ? rows.offset(ph[blk], b, hk, t0) : 0;
-                const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows.kbase + off, (uint32_t)nvalid * kD * 2);
-                const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows.vbase + off, (uint32_t)nvalid * kD * 2);
+                f32x4 acc = f32x4{};
 #pragma unroll
                 for (int ds = 0; ds < 4; ++ds)
-                    kr[blk][ds] = __builtin_amdgcn_raw_buffer_load_b128(
-                        krs, (uint32_t)(c * kD + 32 * ds + 8 * q4) * 2, 0, kStreamAux);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[blk][ds]),
+                                                                   qf[hb][ds], acc, 0, 0, 0);
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    vr[blk][rr] = __builtin_amdgcn_raw_buffer_load_b128(
-                        vrs, (uint32_t)((4 * q4 + rr) * kD + 8 * c) * 2, 0, kStreamAux);
-            }
-        };
-
-        auto process = [&](const Buf& kr, const Buf& vr, int ci) {
-            bf16x4 pf[NHB][2];
-#pragma unroll
-            for (int hb = 0; hb < NHB; ++hb) {
-                float s[2][4];
-#pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
-                    f32x4 acc = f32x4{};
-#pragma unroll
-                    for (int ds = 0; ds < 4; ++ds)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[blk][ds]),
-                                                                       qf[hb][ds], acc, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = c0 + ci * kChunk + 16 * blk + 4 * q4 + r;
-                        s[blk][r] = (key >= p0 && key < p1) ? acc[r] : -INFINITY;
-                    }
-                }
-                float tmax = s[0][0];
-#pragma unroll
-                for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[blk][r]);
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
-                const bool raise = tmax > ref[hb] + kRescaleSlack;
-                if (__builtin_amdgcn_ballot_w64(raise)) {      // wavefront-uniform branch
-                    const float ref_new = raise ? tmax : ref[hb];
-                    const float alpha = exp2_fast(ref[hb] - ref_new);
-                    ref[hb] = ref_new;
-                    lsum[hb] *= alpha;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) oacc[hb][j] *= alpha;
-                }
-#pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
-                    float p[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        p[r] = exp2_fast(fmaf(s[blk][r], scale_log2, -ref[hb]));
-                        lsum[hb] += p[r];
-                    }
-                    u32x2 x;
-                    x.x = pack_bf16x2(p[0], p[1]);
-                    x.y = pack_bf16x2(p[2], p[3]);
-                    pf[hb][blk] = __builtin_bit_cast(bf16x4, x);
+                for (int r = 0; r < 4; ++r) {
+                    const int key = cur.c0 + ci * kChunk + 16 * blk + 4 * q4 + r;
+                    s[blk][r] = (key >= cur.p0 && key < cur.p1) ? acc[r] : -INFINITY;
                 }
             }
-            // O^T += V^T . P^T; MFMA j covers d = 8*m + j.
+            float tmax = s[0][0];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[blk][r]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+            const bool raise = tmax > ref[hb] + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise)) {      // wavefront-uniform branch
+                const float ref_new = raise ? tmax : ref[hb];
+                const float alpha = exp2_fast(ref[hb] - ref_new);
+                ref[hb] = ref_new;
+                lsum[hb] *= alpha;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) oacc[hb][j] *= alpha;
+            }
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
+                float p[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int dw = j >> 1;
-                    u32x2 a;
-                    if (j & 1) {
-                        a.x = pack_hi16(vr[blk][0][dw], vr[blk][1][dw]);
-                        a.y = pack_hi16(vr[blk][2][dw], vr[blk][3][dw]);
-                    } else {
-                        a.x = pack_lo16(vr[blk][0][dw], vr[blk][1][dw]);
-                        a.y = pack_lo16(vr[blk][2][dw], vr[blk][3][dw]);
-                    }
-                    const bf16x4 av = __builtin_bit_cast(bf16x4, a);
-#pragma unroll
-                    for (int hb = 0; hb < NHB; ++hb)
-                        oacc[hb][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pf[hb][blk], oacc[hb][j], 0, 0, 0);
+                for (int r = 0; r < 4; ++r) {
+                    p[r] = exp2_fast(fmaf(s[blk][r], scale_log2, -ref[hb]));
+                    lsum[hb] += p[r];
                 }
+                u32x2 x;
+                x.x = pack_bf16x2(p[0], p[1]);
+                x.y = pack_bf16x2(p[2], p[3]);
+                pf[hb][blk] = __builtin_bit_cast(bf16x4, x);
             }
-        };
-
-        Buf ka, va, kb, vb;
-        int pha[2], phb[2];
-        lookup(pha, 0);
-        lookup(phb, 1);
-        wait_all_memory();             // q fragments and table entries are in registers
-        load(ka, va, pha, 0);
-        for (int ci = 0; ci < nchunks; ci += 2) {
-            lookup(pha, ci + 2);
-            load(kb, vb, phb, ci + 1);
-            process(ka, va, ci);
-            lookup(phb, ci + 3);
-            load(ka, va, pha, ci + 2);
-            if (ci + 1 < nchunks) process(kb, vb, ci + 1);
         }
+        // O^T += V^T . P^T; MFMA j covers d = 8*m + j.
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int dw = j >> 1;
+                u32x2 a;
+                if (j & 1) {
+                    a.x = pack_hi16(vr[blk][0][dw], vr[blk][1][dw]);
+                    a.y = pack_hi16(vr[blk][2][dw], vr[blk][3][dw]);
+                } else {
+                    a.x = pack_lo16(vr[blk][0][dw], vr[blk][1][dw]);
+                    a.y = pack_lo16(vr[blk][2][dw], vr[blk][3][dw]);
+                }
+                const bf16x4 av = __builtin_bit_cast(bf16x4, a);
+#pragma unroll
+                for (int hb = 0; hb < NHB; ++hb)
+                    oacc[hb][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pf[hb][blk], oacc[hb][j], 0, 0, 0);
+            }
+        }
+    };
 
-        // Finish the piece: each lane summed its own keys; the four lanes of a
-        // head share its reference.  Lane holds head hb*16 + c, d = 32*q4 + 8*r + j.
+    // Finish a piece: each lane summed its own keys; the four lanes of a head
+    // share its reference.  Lane holds head hb*16 + c, d = 32*q4 + 8*r + j.
+    auto finish = [&](const Piece& cur) {
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             float lt = lsum[hb] + __shfl_xor(lsum[hb], 16, 64);
             lt += __shfl_xor(lt, 32, 64);
             const int hl = hb * 16 + c;
             if (hl < g) {
-                const size_t row = ((size_t)b * Hq + hk * g + hl) * P + slot;
+                const size_t row = ((size_t)cur.b * Hq + cur.hk * g + hl) * P + cur.slot;
                 const float inv = 1.f / lt;
                 float* dst = opart + row * kD + 32 * q4;
 #pragma unroll
@@ -319,42 +337,126 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                 if (q4 == 0) lsepart[row] = ref[hb] + __builtin_amdgcn_logf(lt);   // v_log_f32: log2
             }
         }
+    };
+
+    // Two chunk buffers (chunk x of a piece in buffer x % 2) with their table
+    // entries.
+    Buf ka, va, kb, vb;
+    int pha[2], phb[2];
+    auto pair = [&](const Piece& cur, const Piece& nxt, int ci, bool last) {
+        lookup(pha, src_of(cur, nxt, ci + 2));
+        load(kb, vb, phb, src_of(cur, nxt, ci + 1));
+        process(ka, va, cur, ci);
+        lookup(phb, src_of(cur, nxt, ci + 3));
+        // The last pair also fetches the next piece's Q fragments (into qn)
+        // with its chunk 0, in straight-line code after the loop, so the wait
+        // before qf takes them over counts only what follows.
+        if (last) load_q(qn, nxt);
+        load(ka, va, pha, src_of(cur, nxt, ci + 2));
+        if (ci + 1 < cur.nchunks) process(kb, vb, cur, ci + 1);
+    };
+
+    Piece cur = describe(start);
+    load_q(qf, cur);
+    lookup(pha, src_of(cur, none, 0));
+    lookup(phb, src_of(cur, none, 1));
+    load(ka, va, pha, src_of(cur, none, 0));
+    for (;;) {
+        const bool more = cur.next < end;
+        const Piece nxt = more ? describe(cur.next) : none;   // none: q of head 0, no K/V
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            ref[hb] = -INFINITY;
+            lsum[hb] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) oacc[hb][j] = f32x4{};
+        }
+        const int last = ((cur.nchunks + 1) & ~1) - 2;
+        for (int ci = 0; ci < last; ci += 2) pair(cur, nxt, ci, false);
+        pair(cur, nxt, last, true);
+        finish(cur);
+        if (!more) break;
+        cur = nxt;
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+            for (int ds = 0; ds < 4; ++ds) qf[hb][ds] = qn[hb][ds];
     }
 }
 
-// One wavefront per (query head, sequence); lane owns d = 2*lane, 2*lane+1.
-__global__ __launch_bounds__(64) void decode_combine_kernel(
+// One workgroup of kCombineWaves wavefronts per (query head, sequence); lane
+// owns d = 2*lane, 2*lane+1.  Wavefront w merges partials w, w + kCombineWaves,
+// ... in one pass with a running maximum (the rescale step of the tiled
+// online softmax), issuing the loads of several partials at once; the
+// wavefronts' results are then merged in LDS in a fixed order.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineBatch = 4;         // partials in flight per wavefront
+
+__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ lsepart, const long long* __restrict__ prefix,
     uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW) {
+    __shared__ float red[kCombineWaves][2][64 + 1];
+    __shared__ float red_m[kCombineWaves], red_den[kCombineWaves];
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int Hkv = Hq / g;
     const long long L = prefix[b + 1] - prefix[b];
-    float o0 = 0.f, o1 = 0.f;
+    float m = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f;
     if (L > 0) {
         const long long W = prefix[B] * Hkv;
         const long long Q = share_tokens(W, NW);
         const long long S = prefix[b] * Hkv + (long long)(hq / g) * L;
         const int np = (int)((S + L - 1) / Q - S / Q) + 1;
         const size_t row0 = ((size_t)b * Hq + hq) * P;
-        float M = -INFINITY;
-        for (int s = lane; s < np; s += 64) M = fmaxf(M, lsepart[row0 + s]);
+        for (int s0 = wave; s0 < np; s0 += kCombineWaves * kCombineBatch) {
+            float x[kCombineBatch];
+            float2 v[kCombineBatch];
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-        float den = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < np; ++s) {
-            const float wgt = exp2_fast(lsepart[row0 + s] - M);
-            const float2 x = *reinterpret_cast<const float2*>(opart + (row0 + s) * kD + 2 * lane);
-            den += wgt;
-            a0 += wgt * x.x;
-            a1 += wgt * x.y;
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const int s = s0 + u * kCombineWaves;
+                const int sc = s < np ? s : np - 1;
+                x[u] = s < np ? lsepart[row0 + sc] : -INFINITY;
+                v[u] = *reinterpret_cast<const float2*>(opart + (row0 + sc) * kD + 2 * lane);
+            }
+#pragma unroll
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const float mn = fmaxf(m, x[u]);
+                const float sc = mn == m ? 1.f : exp2_fast(m - mn);
+                const float wgt = x[u] == -INFINITY ? 0.f : exp2_fast(x[u] - mn);
+                den = den * sc + wgt;
+                a0 = a0 * sc + wgt * v[u].x;
+                a1 = a1 * sc + wgt * v[u].y;
+                m = mn;
+            }
         }
-        o0 = a0 / den;
-        o1 = a1 / den;
     }
-    reinterpret_cast<uint32_t*>(o + ((size_t)b * Hq + hq) * kD)[lane] = pack_bf16x2(o0, o1);
+    red[wave][0][lane] = a0;
+    red[wave][1][lane] = a1;
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_den[wave] = den;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float M = red_m[0];
+#pragma unroll
+        for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red_m[w]);
+        float dt = 0.f, o0 = 0.f, o1 = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kCombineWaves; ++w) {
+                const float f = red_m[w] == -INFINITY ? 0.f : exp2_fast(red_m[w] - M);
+                dt += f * red_den[w];
+                o0 += f * red[w][0][lane];
+                o1 += f * red[w][1][lane];
+            }
+            o0 /= dt;
+            o1 /= dt;
+        }
+        reinterpret_cast<uint32_t*>(o + ((size_t)b * Hq + hq) * kD)[lane] = pack_bf16x2(o0, o1);
+    }
 }
 
 template <int NHB, class Rows>
@@ -377,7 +479,7 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
                        a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(64), 0, stream, opart, lsepart, prefix,
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(64 * kCombineWaves), 0, stream, opart, lsepart, prefix,
                        static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
     return hipGetLastError();
 }
