@@ -17,10 +17,11 @@
 // the length mix.  A share crossing segment boundaries (a segment = one K/V
 // head of one sequence) is processed piece by piece; each piece ends in one
 // partial result (normalised output + base-2 log-sum-exp for the g query
-// heads of the group).  Within a piece the wavefront streams 32-token chunks,
-// double-buffered: chunk i+1 is loaded (non-temporal, range-checked buffer
-// loads, no branches) while chunk i is computed; an online softmax runs across
-// chunks.  Per 16-token block:
+// heads of the group).  The wavefront streams 32-token chunks, double-buffered
+// across its whole share: chunk i+1 is loaded (non-temporal, range-checked
+// buffer loads, no branches) while chunk i is computed, and the next piece's
+// first chunk and Q fragments are fetched while the current piece finishes;
+// an online softmax runs across the chunks of a piece.  Per 16-token block:
 //   S^T (16 keys x 16 heads) = K (16 x d) . Q^T (d x 16)    v_mfma_f32_16x16x32_bf16
 //   O^T (d x 16 heads)      += V^T (d x 16 keys) . P^T      v_mfma_f32_16x16x16_bf16
 // Lane i (c = i%16, q4 = i/16) loads K row c of the block (contraction over d)
@@ -30,10 +31,10 @@
 // the P^T operand: no LDS traffic, no cross-lane traffic.
 //
 // Kernel 2 (combine): per (sequence, query head) finds the partials of its
-// segment from the same share arithmetic and merges them with weights
-// 2^(lse_s - max lse), the rescale step of the tiled online softmax
-// [Attention variants deep-dive, §6.2 forward pseudocode] applied across
-// pieces, and writes bf16.  Fixed work assignment and reduction order: results
+// segment from the same share arithmetic and merges them in one pass with a
+// running maximum, weights 2^(lse_s - max), the rescale step of the tiled
+// online softmax [Attention variants deep-dive, §6.2 forward pseudocode]
+// applied across pieces, and writes bf16.  Fixed work assignment and reduction order: results
 // are bitwise reproducible, and paged == contiguous bitwise for equal contents.
 #include "common.hpp"
 #include "launch.hpp"
