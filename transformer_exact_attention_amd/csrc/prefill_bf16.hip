@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         if (pos < Sq) {
             const int head = hk * g + (r & (g - 1));
             uint16_t* const dst = o + (((size_t)b * Hq + head) * Sq + pos) * D + 8 * m;
-            *reinterpret_cast<u32x4*>(dst) = w;
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));   // written once, never re-read here
         }
     }
 }
