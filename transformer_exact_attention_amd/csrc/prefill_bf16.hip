@@ -249,16 +249,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     };
 
     bf16x8 qa[2][kDSteps];   // filled from q_s once the loads have landed
-    // Zero the K/V tiles (the first step also multiplies a zero P by V
-    // buffer 2), then start K tiles 0, 1 and V tile 0.
+    // Zero what no load may write before it is read: V buffer 2 (the first
+    // step multiplies a zero P by it) and, when the last tile is partial
+    // (its rows past kend are not fetched), every K/V buffer.  Rows past the
+    // last tile that later steps read keep earlier, finite contents.
+    const bool partial = (kend & (kBc - 1)) != 0;
     for (int i = tid; i < kBc * D / 8; i += kThreads) {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        ((lds_u32x4*)(lds_char*)k_s0)[i] = z;
-        ((lds_u32x4*)(lds_char*)k_s1)[i] = z;
-        ((lds_u32x4*)(lds_char*)k_s2)[i] = z;
-        ((lds_u32x4*)(lds_char*)v_s0)[i] = z;
-        ((lds_u32x4*)(lds_char*)v_s1)[i] = z;
         ((lds_u32x4*)(lds_char*)v_s2)[i] = z;
+        if (partial) {
+            ((lds_u32x4*)(lds_char*)k_s0)[i] = z;
+            ((lds_u32x4*)(lds_char*)k_s1)[i] = z;
+            ((lds_u32x4*)(lds_char*)k_s2)[i] = z;
+            ((lds_u32x4*)(lds_char*)v_s0)[i] = z;
+            ((lds_u32x4*)(lds_char*)v_s1)[i] = z;
+        }
     }
     __syncthreads();
     // Q rows of the workgroup -> LDS by direct loads (16 lanes per row, so

@@ -1,11 +1,16 @@
 // fp32 attention forward (VALU FMA, no reduced precision anywhere).
 //
 // Tiled exact attention with an online softmax [Attention variants deep-dive,
-// §6.2 forward pseudocode]: one wavefront owns 64 query rows of one query
-// head, K/V tiles of the head's K/V group are staged in LDS, scores never leave
-// registers.  Each lane owns one query row: its running max, running sum and
-// output accumulator.  K/V head of query head h is h / g [Attention variants
+// §6.2 forward pseudocode]: a workgroup owns 16 query rows of one query head,
+// K/V tiles of the head's K/V group are staged in LDS, scores never leave
+// registers.  K/V head of query head h is h / g [Attention variants
 // deep-dive, §5 GQA code: each K/V head repeated g times along the head axis].
+//
+// Sixteen lanes share a query row, each holding D/16 of its dimensions (its
+// slice of q and of the output accumulator): a score is a 16-lane sum of
+// partial dot products, after which every lane of the group holds it and
+// keeps the row's running max and sum.  Per 32-key tile the scores are
+// computed first, then one rescale and the P.V update.
 //
 // This path serves fp32 inputs (small problems: latency-bound); the MFMA path
 // in prefill_bf16.hip is the throughput kernel.
@@ -16,79 +21,88 @@ namespace gqa {
 
 namespace {
 
-constexpr int kRows = 64;      // query rows per workgroup (one per lane)
-constexpr int kKeys = 16;      // keys per LDS tile
+constexpr int kLanesPerRow = 16;
+constexpr int kThreadsF32 = 256;
+constexpr int kRowsF32 = kThreadsF32 / kLanesPerRow;   // query rows per workgroup
+constexpr int kKeysF32 = 32;                           // keys per LDS tile
 
 template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(
+__global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, float scale_log2, int causal) {
-    __shared__ float ks[kKeys][D + 1];
-    __shared__ float vs[kKeys][D];
+    constexpr int DL = D / kLanesPerRow;               // dimensions per lane
+    __shared__ float ks[kKeysF32][D + 4];
+    __shared__ float vs[kKeysF32][D + 4];
 
-    const int lane = threadIdx.x;
-    const int row0 = blockIdx.x * kRows;
+    const int tid = threadIdx.x;
+    const int sub = tid & (kLanesPerRow - 1);          // dimension slice of this lane
+    const int row0 = blockIdx.x * kRowsF32;
+    const int row = row0 + tid / kLanesPerRow;
     const int h = blockIdx.y;
     const int b = blockIdx.z;
     const int g = Hq / Hkv;
     const int hk = h / g;
-    const int row = row0 + lane;
     const bool live = row < Sq;
 
     const size_t qoff = ((size_t)(b * Hq + h) * Sq) * D;
     const size_t kvoff = ((size_t)(b * Hkv + hk) * Sk) * D;
 
-    float qr[D];
-    float acc[D];
+    float qr[DL], acc[DL];
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
-        qr[c] = live ? q[qoff + (size_t)row * D + c] : 0.f;
-        acc[c] = 0.f;
+    for (int i = 0; i < DL; ++i) {
+        qr[i] = live ? q[qoff + (size_t)row * D + sub * DL + i] : 0.f;
+        acc[i] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
 
     // Keys this workgroup can see: causal rows see j <= row + (Sk - Sq).
     int kend = Sk;
     if (causal) {
-        const int last_row = min(row0 + kRows, Sq) - 1;
+        const int last_row = min(row0 + kRowsF32, Sq) - 1;
         kend = min(Sk, last_row + (Sk - Sq) + 1);
     }
     const int my_last = causal ? row + (Sk - Sq) : Sk - 1;
 
-    for (int j0 = 0; j0 < kend; j0 += kKeys) {
+    for (int j0 = 0; j0 < kend; j0 += kKeysF32) {
         __syncthreads();
-        for (int e = lane; e < kKeys * D; e += 64) {
-            const int r = e / D, c = e % D;
+        for (int e = tid; e < kKeysF32 * D / 4; e += kThreadsF32) {
+            const int r = e / (D / 4), c = 4 * (e % (D / 4));
             const bool in = (j0 + r) < Sk;
-            ks[r][c] = in ? k[kvoff + (size_t)(j0 + r) * D + c] : 0.f;
-            vs[r][c] = in ? v[kvoff + (size_t)(j0 + r) * D + c] : 0.f;
+            const float4 kz = in ? *reinterpret_cast<const float4*>(k + kvoff + (size_t)(j0 + r) * D + c)
+                                 : float4{0.f, 0.f, 0.f, 0.f};
+            const float4 vz = in ? *reinterpret_cast<const float4*>(v + kvoff + (size_t)(j0 + r) * D + c)
+                                 : float4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<float4*>(&ks[r][c]) = kz;
+            *reinterpret_cast<float4*>(&vs[r][c]) = vz;
         }
         __syncthreads();
 
-        float s[kKeys];
+        float s[kKeysF32];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < kKeys; ++r) {
+        for (int r = 0; r < kKeysF32; ++r) {
             float dot = 0.f;
 #pragma unroll
-            for (int c = 0; c < D; ++c) dot = fmaf(qr[c], ks[r][c], dot);
+            for (int i = 0; i < DL; ++i) dot = fmaf(qr[i], ks[r][sub * DL + i], dot);
+#pragma unroll
+            for (int x = 1; x < kLanesPerRow; x <<= 1) dot += __shfl_xor(dot, x, 64);
             const int j = j0 + r;
             const bool vis = (j < Sk) && (j <= my_last);
             s[r] = vis ? dot * scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, s[r]);
         }
         const float m_new = fmaxf(m, tmax);
-        if (m_new == -INFINITY) continue;           // nothing visible yet for this row
-        const float alpha = exp2f(m - m_new);       // 0 when m == -inf
+        if (m_new == -INFINITY) continue;              // nothing visible yet for this row
+        const float alpha = exp2f(m - m_new);          // 0 when m == -inf
         l *= alpha;
 #pragma unroll
-        for (int c = 0; c < D; ++c) acc[c] *= alpha;
+        for (int i = 0; i < DL; ++i) acc[i] *= alpha;
 #pragma unroll
-        for (int r = 0; r < kKeys; ++r) {
+        for (int r = 0; r < kKeysF32; ++r) {
             const float p = exp2f(s[r] - m_new);
             l += p;
 #pragma unroll
-            for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vs[r][c], acc[c]);
+            for (int i = 0; i < DL; ++i) acc[i] = fmaf(p, vs[r][sub * DL + i], acc[i]);
         }
         m = m_new;
     }
@@ -96,24 +110,24 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
     if (live) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int c = 0; c < D; ++c) o[qoff + (size_t)row * D + c] = acc[c] * inv;
+        for (int i = 0; i < DL; ++i) o[qoff + (size_t)row * D + sub * DL + i] = acc[i] * inv;
     }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
-    dim3 grid((a.Sq + kRows - 1) / kRows, a.Hq, a.B);
+    dim3 grid((a.Sq + kRowsF32 - 1) / kRowsF32, a.Hq, a.B);
     const float sl = a.scale * kLog2e;
     const float* q = static_cast<const float*>(a.q);
     const float* k = static_cast<const float*>(a.k);
     const float* v = static_cast<const float*>(a.v);
     float* o = static_cast<float*>(a.o);
     if (a.d == 64)
-        hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, o, a.Hq, a.Hkv,
+        hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv,
                            a.Sq, a.Sk, sl, a.causal);
     else
-        hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, o, a.Hq, a.Hkv,
+        hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv,
                            a.Sq, a.Sk, sl, a.causal);
     return hipGetLastError();
 }
