@@ -153,7 +153,7 @@ __device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, int lg, int nqb,
+    uint16_t* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, int lg, int nqb, int by_cost,
     float scale_log2, int causal) {
     constexpr int kChunks = D / 8;                          // 16-byte chunks per row
     constexpr int kDSteps = D / 16;                         // MFMA contraction steps over d
@@ -187,11 +187,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // workgroup id L runs on XCD L % 8; when the item count divides by 8, XCD x
     // is given the contiguous item range [x * N/8, (x+1) * N/8): whole planes,
     // whose K/V then stay in that XCD's L2 instead of being fetched by all 8.
+    // With by_cost (planes too short to fill an XCD), the XCD's items are
+    // handed out heaviest query block first across all of its planes, so the
+    // CUs that start with light items do not meet heavy ones at the end.
     const int nitems = (int)gridDim.x;
     const int L = (int)blockIdx.x;
-    const int item = (nitems & 7) == 0 ? (L & 7) * (nitems >> 3) + (L >> 3) : L;
-    const int plane = item / nqb;
-    const int qb = nqb - 1 - (item - plane * nqb);
+    int plane, qb;
+    if (by_cost) {
+        const int ppx = nitems / (8 * nqb);               // planes per XCD
+        const int j = L >> 3;
+        plane = (L & 7) * ppx + j % ppx;
+        qb = nqb - 1 - j / ppx;
+    } else {
+        const int item = (nitems & 7) == 0 ? (L & 7) * (nitems >> 3) + (L >> 3) : L;
+        plane = item / nqb;
+        qb = nqb - 1 - (item - plane * nqb);
+    }
     const int hk = plane % Hkv;
     const int b = plane / Hkv;
     const int p0 = qb * npos;
@@ -661,16 +672,24 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int nqb = (a.Sq + npos - 1) / npos;
     dim3 grid(nqb * a.Hkv * a.B);
     const float sl = a.scale * kLog2e;
+    // Order items by cost across planes when a plane has fewer query blocks
+    // than an XCD has CUs (8 XCDs; needs a plane count divisible by 8).
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+    const int nplanes = a.Hkv * a.B;
+    const int by_cost = (nplanes % 8 == 0) && (nqb * 8 < cus) ? 1 : 0;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
     uint16_t* o = static_cast<uint16_t*>(a.o);
     if (a.d == 64)
         hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v, o, a.Hq,
-                           a.Hkv, a.Sq, a.Sk, lg, nqb, sl, a.causal);
+                           a.Hkv, a.Sq, a.Sk, lg, nqb, by_cost, sl, a.causal);
     else
         hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v, o, a.Hq,
-                           a.Hkv, a.Sq, a.Sk, lg, nqb, sl, a.causal);
+                           a.Hkv, a.Sq, a.Sk, lg, nqb, by_cost, sl, a.causal);
     return hipGetLastError();
 }
 
