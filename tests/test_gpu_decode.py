@@ -66,6 +66,29 @@ def test_decode_small(ga, Hq, Hkv, paged):
     assert_close(got, ref, "bf16", "decode small")
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_many_short_sequences(ga, paged):
+    # The largest supported batch (4096 sequences, the prefix sums live in LDS)
+    # with short and empty sequences: every wavefront's share crosses dozens
+    # of (sequence, K/V head) segments, so the pipeline runs across many
+    # piece boundaries and the combine meets segments of one or two pieces.
+    B, Hq, Hkv = 4096, 8, 2
+    lens = np.random.default_rng(44).integers(0, 41, B).astype(np.int32)
+    lens[::97] = 0
+    note(f"decode many short sequences B{B} paged={paged}")
+    q, kc, vc, lens, table = small_case(44, B, Hq, Hkv, lens, 48, paged)
+    if paged:
+        o = run_paged(ga, q, kc, vc, lens, table, max_seq_len=48)
+        ref = oracle.decode_paged(ref_f64(q, "bf16"), ref_f64(kc, "bf16"), ref_f64(vc, "bf16"), table, lens)
+    else:
+        o = run_contig(ga, q, kc, vc, lens)
+        ref = oracle.decode_contiguous(ref_f64(q, "bf16"), ref_f64(kc, "bf16"), ref_f64(vc, "bf16"), lens)
+    got = to_f64(o)
+    assert np.all(got[lens == 0] == 0)
+    # (short sequences: outputs are close to single V rows, |O| up to ~4)
+    assert_close(got, ref, "bf16", "decode many short sequences", beyond_unit=True)
+
+
 def test_decode_single_token_returns_value_row(ga):
     import torch
     q, kc, vc, lens, _ = small_case(40, 3, 8, 2, [1, 1, 1], 32, False)
