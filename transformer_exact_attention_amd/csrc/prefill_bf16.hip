@@ -365,8 +365,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     float ref[2] = {-INFINITY, -INFINITY};   // reference max, scaled base-2 units
     float l[2] = {0.f, 0.f};                 // running sum over this lane's keys
 
-    wait_all_memory();
-    __syncthreads();
+    // Q and K tile 0 have landed (loads complete in issue order); K tile 1
+    // and V tile 0 may still be in flight: the first step waits for them.
+    wait_vmcnt<2 * kTileLoads>();
+    lds_barrier();
     // Q^T operand fragments of this lane's two query columns: Q[row][16t +
     // 8hh .. +8] for d-step t, kept in AGPRs.
 #pragma unroll
@@ -387,9 +389,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         u32x4 r[2];     // QK: K rows n, 32+n
         s16x4 t[4];     // PV: lo/hi of d-tile 0, lo/hi of d-tile 1
     };
-    auto group_reads = [](int gi) { return (gi & 1) == 0 ? 2 : 4; };
+    auto group_reads = [](int gi) { return (gi & 1) == 0 ? 4 : 2; };
     auto issue_read = [&](const uint16_t* ks, const uint16_t* vs, int x, int gi, int r, Ops& op) {
-        if ((gi & 1) == 0) {
+        if ((gi & 1) != 0) {
             const int t = kStepsPerWindow * x + (gi >> 1);
             op.r[r] = *(lds_u32x4*)((lds_char*)ks + k_byte<D>(n + 32 * r, 2 * t + hh));
         } else {
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
     };
     auto group_mfma = [&](int x, int gi, int m, const Ops& op, f32x16 (&sacc)[2][2]) {
-        if ((gi & 1) == 0) {
+        if ((gi & 1) != 0) {
             const int t = kStepsPerWindow * x + (gi >> 1);
             const int nb = m >> 1, kb = m & 1;
             qk_mfma(sacc[nb][kb], op.r[kb], qa[nb][t], t == 0);
@@ -424,28 +426,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         const uint16_t* const k_read = ks[(PAR + 1) % 3];  // tile j+1
         const uint16_t* const v_read = vs[(PAR + 2) % 3];  // tile j-1
 
-        // The previous step's loads have landed, and every wavefront is done
-        // with the buffers refilled during this step.  The loads are issued
-        // from the main block below, also past the last tile (keys are
-        // clamped), which keeps that block free of branches.
-        wait_vmcnt<0>();
-        lds_barrier();
-        int wave_lds = 1024 * wave_u;
-        asm volatile("" : "+s"(wave_lds));
-
         // The main block below is scheduled by hand, one slot at a time: an
         // MFMA, the vector work of one or two softmax elements, and one LDS
         // read of the next 4-MFMA group, fenced so the compiler keeps the
-        // order.  Groups alternate between a score step of tile j+1 (QK) and
-        // two d-tiles of the P.V product of tile j-1 (PV); the operands of a
+        // order.  Groups alternate between two d-tiles of the P.V product of
+        // tile j-1 (PV) and a score step of tile j+1 (QK); the operands of a
         // group are read during the group before it.
         constexpr int kGroups = 2 * kStepsPerWindow;        // 4-MFMA groups per window
         constexpr int kElems = 16 / (4 * kGroups);          // softmax elements per slot
         // Operands are read kAhead groups ahead of their MFMAs.
         constexpr int kAhead = 2;
         Ops ops[kAhead + 1];
+        // The first group, P.V of tile j-1, reads a V tile that is resident
+        // since the previous barrier and is not refilled in this step: its
+        // operands are read before the barrier, so the matrix cores start as
+        // soon as it opens.
 #pragma unroll
-        for (int ga = 0; ga < kAhead; ++ga)
+        for (int r = 0; r < group_reads(0); ++r) issue_read(k_read, v_read, 0, 0, r, ops[0]);
+        // After the barrier the previous step's loads have landed, and every
+        // wavefront is done with the buffers refilled during this step.  The
+        // loads are issued from the main block below, also past the last tile
+        // (keys are clamped), which keeps that block free of branches.
+        wait_vmcnt<0>();
+        lds_barrier();
+        int wave_lds = 1024 * wave_u;
+        asm volatile("" : "+s"(wave_lds));
+#pragma unroll
+        for (int ga = 1; ga < kAhead; ++ga)
 #pragma unroll
             for (int r = 0; r < group_reads(ga % kGroups); ++r)
                 issue_read(k_read, v_read, ga / kGroups, ga % kGroups, r, ops[ga]);
