@@ -18,8 +18,9 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; tensors are
  *    dense, row-major, with the layouts stated per call.  The library never
- *    allocates or frees memory and keeps no mutable global state; calls are
- *    reentrant.
+ *    allocates or frees device memory and keeps no mutable global state
+ *    (the only memory it allocates is a KV pool's host-side bookkeeping,
+ *    behind the pool's handle: gqa_kv_cache.h); calls are reentrant.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    on it and the call returns before the kernels finish (except
  *    attn_decode_validate, which synchronises).
@@ -44,12 +45,13 @@ typedef enum {
     GQA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, Hq % Hkv != 0, bad scale, ... */
     GQA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head dim, dtype, group size) */
     GQA_ERR_WORKSPACE = 3,     /* decode workspace missing or too small */
-    GQA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+    GQA_ERR_HIP = 4,           /* a HIP launch or runtime call failed */
+    GQA_ERR_OUT_OF_BLOCKS = 5  /* KV pool: not enough free blocks (see gqa_kv_cache.h) */
 } gqa_status;
 
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
 
-#define GQA_ATTN_ABI_VERSION 1
+#define GQA_ATTN_ABI_VERSION 2
 #define GQA_PAGE_BLOCK_SIZE 16   /* tokens per KV page */
 
 /* Version of this ABI (GQA_ATTN_ABI_VERSION of the built library). */

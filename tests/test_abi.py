@@ -8,12 +8,17 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+|void\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text,
+                                re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -25,7 +30,10 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
-                            "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate"])
+                            "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate",
+                            "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks",
+                            "gqa_kv_seq_new", "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len",
+                            "gqa_kv_reserve", "gqa_kv_block_table", "attn_kv_append", "attn_kv_copy_blocks"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -38,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_abi_version_and_status_strings(lib):
     ver = int(re.search(r"#define GQA_ATTN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert lib.gqa_attn_abi_version() == ver
-    for s in range(5):
+    for s in range(6):
         assert lib.gqa_attn_status_string(s)
     assert lib.gqa_attn_status_string(99) == b"unknown status"
 

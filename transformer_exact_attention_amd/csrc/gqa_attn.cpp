@@ -1,7 +1,7 @@
 // C ABI of libgqa_attn: host-side validation, planning and kernel launch.
 //
 // Every check runs on the host before the first HIP call, so a rejected call
-// enqueues nothing.  The library allocates nothing and keeps no state.
+// enqueues nothing.  These calls allocate nothing and keep no state.
 #include "../../include/gqa_attn.h"
 
 #include <hip/hip_runtime.h>
@@ -89,6 +89,7 @@ const char* gqa_attn_status_string(int status) {
         case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
         case GQA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
         case GQA_ERR_HIP: return "HIP runtime error";
+        case GQA_ERR_OUT_OF_BLOCKS: return "KV pool exhausted (free blocks or sequence ids)";
         default: return "unknown status";
     }
 }

@@ -65,8 +65,28 @@ inline size_t decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
     return decode_workspace_layout(B, Hq, d, max_seq_len).total;
 }
 
+// Paged KV cache: new tokens [n_tokens, Hkv, d] to their slots, and whole
+// block copies; rows are row_bytes = d * element size bytes (16 | row_bytes).
+struct KvAppendArgs {
+    void* k_cache;
+    void* v_cache;
+    const void* k_new;
+    const void* v_new;
+    const int32_t* slots;
+    int n_tokens, num_blocks, Hkv, row_bytes;
+};
+struct KvCopyArgs {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* src;
+    const int32_t* dst;
+    int n, num_blocks, Hkv, row_bytes;
+};
+
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+hipError_t launch_kv_copy_blocks(const KvCopyArgs& a, hipStream_t stream);
 
 }  // namespace gqa

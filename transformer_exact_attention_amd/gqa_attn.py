@@ -19,18 +19,25 @@ import torch  # noqa: F401  (loads the HIP runtime the library shares)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
 
-GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(5)
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP, GQA_ERR_OUT_OF_BLOCKS = range(6)
 GQA_F32, GQA_BF16 = 0, 1
 PAGE_BLOCK_SIZE = 16
 
 EXPORTS = ("gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
-           "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate")
+           "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate",
+           "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks", "gqa_kv_seq_new",
+           "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len", "gqa_kv_reserve", "gqa_kv_block_table",
+           "attn_kv_append", "attn_kv_copy_blocks")
 
 _lib = None
 
 
 class GqaAttnError(RuntimeError):
     pass
+
+
+class OutOfBlocksError(GqaAttnError):
+    """A KV pool has too few free blocks (or sequence ids) for the request."""
 
 
 def load_library(path: str = LIB_PATH):
@@ -55,6 +62,29 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, vp, c_size, vp]
     lib.attn_decode_validate.restype = c_int
     lib.attn_decode_validate.argtypes = [vp, vp] + [c_int] * 5 + [vp]
+    ip = ctypes.POINTER(c_int)
+    lib.gqa_kv_pool_create.restype = c_int
+    lib.gqa_kv_pool_create.argtypes = [c_int, c_int, c_int, ctypes.POINTER(vp)]
+    lib.gqa_kv_pool_destroy.restype = None
+    lib.gqa_kv_pool_destroy.argtypes = [vp]
+    lib.gqa_kv_pool_free_blocks.restype = c_int
+    lib.gqa_kv_pool_free_blocks.argtypes = [vp]
+    lib.gqa_kv_seq_new.restype = c_int
+    lib.gqa_kv_seq_new.argtypes = [vp, ip]
+    lib.gqa_kv_seq_fork.restype = c_int
+    lib.gqa_kv_seq_fork.argtypes = [vp, c_int, ip]
+    lib.gqa_kv_seq_release.restype = c_int
+    lib.gqa_kv_seq_release.argtypes = [vp, c_int]
+    lib.gqa_kv_seq_len.restype = c_int
+    lib.gqa_kv_seq_len.argtypes = [vp, c_int]
+    lib.gqa_kv_reserve.restype = c_int
+    lib.gqa_kv_reserve.argtypes = [vp, vp, vp, c_int, vp, vp, vp, ip]
+    lib.gqa_kv_block_table.restype = c_int
+    lib.gqa_kv_block_table.argtypes = [vp, vp, c_int, vp, c_int, vp]
+    lib.attn_kv_append.restype = c_int
+    lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 5 + [vp]
+    lib.attn_kv_copy_blocks.restype = c_int
+    lib.attn_kv_copy_blocks.argtypes = [vp, vp, vp, vp] + [c_int] * 5 + [vp]
     _lib = lib
     return lib
 
@@ -75,6 +105,8 @@ def _raise(status: int, what: str):
         raise ValueError(msg)
     if status == GQA_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
+    if status == GQA_ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocksError(msg)
     raise GqaAttnError(msg)
 
 
@@ -213,3 +245,122 @@ def attn_decode_validate(seq_lens: torch.Tensor, block_table: Optional[torch.Ten
     bs = PAGE_BLOCK_SIZE if block_table is not None else 0
     return lib.attn_decode_validate(seq_lens.data_ptr(), block_table.data_ptr() if block_table is not None else None,
                                     B, int(max_seq_len), bs, mb, int(num_physical_blocks), _stream(stream))
+
+
+# ---- paged KV cache (gqa_kv_cache.h) ---------------------------------------
+
+def _host_i32(a, n=None):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    if n is not None and a.shape != (n,):
+        raise ValueError(f"expected {n} int32 values")
+    return a
+
+
+class KVPool:
+    """Host-side page allocator of the library (gqa_kv_pool): page tables,
+    block references, copy-on-write prefix sharing.  Methods carry the C
+    names without the ``gqa_kv_`` prefix; ids and slots are plain ints and
+    int32 numpy arrays."""
+
+    def __init__(self, num_blocks: int, max_seqs: int, max_blocks_per_seq: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _raise(self._lib.gqa_kv_pool_create(int(num_blocks), int(max_seqs), int(max_blocks_per_seq),
+                                            ctypes.byref(h)), "gqa_kv_pool_create")
+        self._h = h
+        self.num_blocks, self.max_seqs, self.max_blocks_per_seq = int(num_blocks), int(max_seqs), int(max_blocks_per_seq)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.gqa_kv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def free_blocks(self) -> int:
+        return int(self._lib.gqa_kv_pool_free_blocks(self._h))
+
+    def seq_new(self) -> int:
+        out = ctypes.c_int()
+        _raise(self._lib.gqa_kv_seq_new(self._h, ctypes.byref(out)), "gqa_kv_seq_new")
+        return out.value
+
+    def seq_fork(self, parent: int) -> int:
+        out = ctypes.c_int()
+        _raise(self._lib.gqa_kv_seq_fork(self._h, int(parent), ctypes.byref(out)), "gqa_kv_seq_fork")
+        return out.value
+
+    def seq_release(self, seq: int):
+        _raise(self._lib.gqa_kv_seq_release(self._h, int(seq)), "gqa_kv_seq_release")
+
+    def seq_len(self, seq: int) -> int:
+        return int(self._lib.gqa_kv_seq_len(self._h, int(seq)))
+
+    def reserve(self, seqs, counts):
+        """Slots for counts[i] new tokens of seqs[i]; returns (slots, copy_src, copy_dst)."""
+        import numpy as np
+        seqs = _host_i32(seqs)
+        counts = _host_i32(counts, seqs.shape[0])
+        n = seqs.shape[0]
+        total = int(counts.sum()) if n else 0
+        slots = np.empty(max(total, 1), dtype=np.int32)
+        src = np.empty(max(n, 1), dtype=np.int32)
+        dst = np.empty(max(n, 1), dtype=np.int32)
+        nc = ctypes.c_int(0)
+        _raise(self._lib.gqa_kv_reserve(self._h, seqs.ctypes.data, counts.ctypes.data, n, slots.ctypes.data,
+                                        src.ctypes.data, dst.ctypes.data, ctypes.byref(nc)), "gqa_kv_reserve")
+        return slots[:total].copy(), src[:nc.value].copy(), dst[:nc.value].copy()
+
+    def block_table(self, seqs, max_blocks: int):
+        """(table int32 [n, max_blocks] padded with -1, lens int32 [n])."""
+        import numpy as np
+        seqs = _host_i32(seqs)
+        n = seqs.shape[0]
+        table = np.empty((n, int(max_blocks)), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        _raise(self._lib.gqa_kv_block_table(self._h, seqs.ctypes.data, n, table.ctypes.data, int(max_blocks),
+                                            lens.ctypes.data), "gqa_kv_block_table")
+        return table, lens
+
+
+def _page_dims(k_cache, v_cache):
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[2] != PAGE_BLOCK_SIZE:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, Hkv, 16, d]")
+    num_blocks, Hkv, _, d = k_cache.shape
+    return num_blocks, Hkv, d
+
+
+def attn_kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   slots: torch.Tensor, stream=None):
+    """Write tokens k_new/v_new [n, Hkv, d] into the pages at slots (int32 [n], device)."""
+    lib = load_library()
+    num_blocks, Hkv, d = _page_dims(k_cache, v_cache)
+    n = k_new.shape[0]
+    if k_new.dim() != 3 or tuple(k_new.shape) != (n, Hkv, d) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new and v_new must both be [n_tokens, Hkv, d]")
+    if slots.dtype != torch.int32 or tuple(slots.shape) != (n,):
+        raise ValueError("slots must be int32 [n_tokens]")
+    if n == 0:
+        return
+    _dev(k_cache, v_cache, k_new, v_new, slots)
+    code = _dtype_code(k_cache, v_cache, k_new, v_new)
+    _raise(lib.attn_kv_append(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                              slots.data_ptr(), n, num_blocks, Hkv, d, code, _stream(stream)), "attn_kv_append")
+
+
+def attn_kv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
+                        stream=None):
+    """Copy whole blocks src[i] -> dst[i] (int32 [n], device) of both caches."""
+    lib = load_library()
+    num_blocks, Hkv, d = _page_dims(k_cache, v_cache)
+    n = src.shape[0]
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.dim() != 1 or tuple(dst.shape) != (n,):
+        raise ValueError("src and dst must be int32 [n]")
+    if n == 0:
+        return
+    _dev(k_cache, v_cache, src, dst)
+    code = _dtype_code(k_cache, v_cache)
+    _raise(lib.attn_kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src.data_ptr(), dst.data_ptr(), n,
+                                   num_blocks, Hkv, d, code, _stream(stream)), "attn_kv_copy_blocks")
