@@ -126,6 +126,32 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode over an fp8 KV cache [Attention variants deep-dive, §7 KV Cache:
+ * fp16 -> fp8 halves the cache; §8 Q4: quantise the KV cache to fp8].  The
+ * same computation as attn_decode_fwd with every cached row standing for
+ * E4M3(code) * row scale:
+ *   k_cache, v_cache : uint8 OCP E4M3 codes (sign, 4 exponent bits with bias
+ *                      7, 3 mantissa bits, largest finite 448), laid out as
+ *                      attn_decode_fwd's bf16 caches: [B, Hkv, max_seq_len, d]
+ *                      or pages [num_blocks, Hkv, 16, d];
+ *   k_scale, v_scale : fp32, one per row: [B, Hkv, max_seq_len] or
+ *                      [num_blocks, Hkv, 16], device;
+ *   q, o             : bf16 [B, Hq, d].
+ * attn_kv_append_fp8 (gqa_kv_cache.h) writes such rows.  Supported and
+ * errors as attn_decode_fwd (bf16 q/o, d == 128); additionally
+ * GQA_ERR_INVALID_ARG for NULL scales and GQA_ERR_UNSUPPORTED for a
+ * contiguous cache whose max_seq_len is not a multiple of 16 (scales are
+ * read 16 rows at a time).  Scales of rows past a sequence's length are read
+ * but never used, so they may hold anything.
+ */
+int attn_decode_fp8_fwd(const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, void* o,
+                        const int32_t* seq_lens, const int32_t* block_table,
+                        int B, int Hq, int Hkv, int d, int max_seq_len,
+                        int block_size, int max_blocks_per_seq, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Debug/test helper (synchronous): copies seq_lens (and block_table, if not
  * NULL) to the host and checks 0 <= seq_lens[b] <= max_seq_len and that every
  * table entry a sequence reads lies in [0, num_physical_blocks).

@@ -140,6 +140,27 @@ int attn_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* 
 int attn_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n,
                         int num_blocks, int Hkv, int d, int dtype, void* stream);
 
+/*
+ * fp8 caches (read by attn_decode_fp8_fwd) [Attention variants deep-dive,
+ * §7 KV Cache: fp16 -> fp8 halves the cache].  Codes are OCP E4M3 (uint8)
+ * in pages [num_blocks, Hkv, 16, d] with one fp32 scale per row in
+ * [num_blocks, Hkv, 16] (k_scale, v_scale).  A row x of d values is stored
+ * as scale = amax / 448 (amax = max |x|) and codes E4M3(x * (448 / amax)),
+ * each fp32 operation rounded to nearest even, each code the nearest E4M3
+ * value with ties to the even code; an all-zero row stores scale 0.
+ *
+ * attn_kv_append_fp8: as attn_kv_append, quantising bf16 k_new, v_new
+ * [n_tokens, Hkv, d]; attn_kv_copy_blocks_fp8: as attn_kv_copy_blocks, also
+ * copying the blocks' scales.  d must be 128 (GQA_ERR_UNSUPPORTED
+ * otherwise); NULL scale arrays are GQA_ERR_INVALID_ARG.
+ */
+int attn_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const void* k_new,
+                       const void* v_new, const int32_t* slots, int n_tokens, int num_blocks, int Hkv, int d,
+                       void* stream);
+
+int attn_kv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const int32_t* src,
+                            const int32_t* dst, int n, int num_blocks, int Hkv, int d, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                             "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate",
                             "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks",
                             "gqa_kv_seq_new", "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len",
-                            "gqa_kv_reserve", "gqa_kv_block_table", "attn_kv_append", "attn_kv_copy_blocks"])
+                            "gqa_kv_reserve", "gqa_kv_block_table", "attn_kv_append", "attn_kv_copy_blocks",
+                            "attn_decode_fp8_fwd", "attn_kv_append_fp8", "attn_kv_copy_blocks_fp8"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -126,3 +127,23 @@ def test_binding_raises_typed_errors_without_touching_the_gpu():
     with pytest.raises(gqa_attn.GqaAttnError):
         gqa_attn._raise(4, "x")
     gqa_attn._raise(0, "x")
+
+
+def decode_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lens=FAKE, table=None, B=2, Hq=8, Hkv=2, d=128,
+             max_seq_len=64, block_size=0, max_blocks=0, scale=0.1, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_fp8_fwd(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], a["lens"], a["table"], a["B"],
+                                   a["Hq"], a["Hkv"], a["d"], a["max_seq_len"], a["block_size"], a["max_blocks"],
+                                   a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), 1), (dict(vs=None), 1), (dict(q=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(scale=-1.0), 1),
+    (dict(d=64), 2), (dict(Hq=96, Hkv=1), 2),
+    (dict(max_seq_len=100), 2),                       # contiguous fp8 caches need max_seq_len % 16 == 0
+    (dict(table=FAKE, block_size=16, max_blocks=2, max_seq_len=64), 1),   # table narrower than max_seq_len
+    (dict(ws=None), 3), (dict(ws_bytes=16), 3),
+])
+def test_decode_fp8_rejects_on_host(lib, kw, status):
+    assert decode_fp8(lib, **kw) == status

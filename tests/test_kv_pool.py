@@ -373,3 +373,26 @@ def test_kv_copy_rejects_on_host(ga, kw, status):
     lib = ga.load_library()
     assert lib.attn_kv_copy_blocks(a["k"], a["v"], a["src"], a["dst"], a["n"], a["num_blocks"], a["Hkv"], a["d"],
                                    a["dtype"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), 1), (dict(vs=None), 1), (dict(k=None), 1), (dict(d=64), 2), (dict(n=-1), 1), (dict(Hkv=0), 1),
+    (dict(n=0), 0),
+])
+def test_kv_append_fp8_rejects_on_host(ga, kw, status):
+    a = dict(k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, kn=FAKE, vn=FAKE, slots=FAKE, n=4, num_blocks=8, Hkv=2, d=128)
+    a.update(kw)
+    lib = ga.load_library()
+    assert lib.attn_kv_append_fp8(a["k"], a["v"], a["ks"], a["vs"], a["kn"], a["vn"], a["slots"], a["n"],
+                                  a["num_blocks"], a["Hkv"], a["d"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), 1), (dict(dst=None), 1), (dict(d=64), 2), (dict(n=-1), 1), (dict(n=0), 0),
+])
+def test_kv_copy_fp8_rejects_on_host(ga, kw, status):
+    a = dict(k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, src=FAKE, dst=FAKE, n=3, num_blocks=8, Hkv=2, d=128)
+    a.update(kw)
+    lib = ga.load_library()
+    assert lib.attn_kv_copy_blocks_fp8(a["k"], a["v"], a["ks"], a["vs"], a["src"], a["dst"], a["n"],
+                                       a["num_blocks"], a["Hkv"], a["d"], None) == status

@@ -65,21 +65,27 @@ __device__ __forceinline__ long long share_tokens(long long W, long long NW) {
     return q < kDecodeMinShare ? kDecodeMinShare : q;
 }
 
-// Row addressing: element offset of the 16 tokens t0..t0+15 (t0 % 16 == 0) of
-// K/V head hk of sequence b; the 16 rows follow each other in both layouts.
+// Row addressing: index of the row holding token t0 (t0 % 16 == 0) of K/V
+// head hk of sequence b; the 16 rows of a block follow each other in both
+// layouts, and the per-row scales of an fp8 cache are indexed by the same
+// row number.
 struct ContiguousRows {
-    const uint16_t* kbase;
-    const uint16_t* vbase;
+    const char* kbase;           // [B, Hkv, S_max, d] elements
+    const char* vbase;
+    const float* kscale;         // fp8 caches: [B, Hkv, S_max]
+    const float* vscale;
     int Hkv, S_max;
     __device__ __forceinline__ int lookup(const int32_t*, int, int) const { return 0; }
-    __device__ __forceinline__ size_t offset(int, int b, int hk, int t0) const {
-        return (((size_t)b * Hkv + hk) * S_max + t0) * kD;
+    __device__ __forceinline__ size_t row(int, int b, int hk, int t0) const {
+        return ((size_t)b * Hkv + hk) * S_max + t0;
     }
 };
 
 struct PagedRows {
-    const uint16_t* kbase;       // pages [num_blocks, Hkv, 16, d]
-    const uint16_t* vbase;
+    const char* kbase;           // pages [num_blocks, Hkv, 16, d]
+    const char* vbase;
+    const float* kscale;         // fp8 caches: [num_blocks, Hkv, 16]
+    const float* vscale;
     int Hkv, max_blocks;
     // Physical block of logical block blk of sequence b, from the block table
     // [B, max_blocks] (a separate restrict kernel argument, so this uniform
@@ -87,12 +93,41 @@ struct PagedRows {
     __device__ __forceinline__ int lookup(const int32_t* __restrict__ table, int b, int blk) const {
         return table[(size_t)b * max_blocks + blk];
     }
-    __device__ __forceinline__ size_t offset(int phys, int, int hk, int) const {
-        return ((size_t)phys * Hkv + hk) * 16 * kD;
+    __device__ __forceinline__ size_t row(int phys, int, int hk, int) const {
+        return ((size_t)phys * Hkv + hk) * 16;
     }
 };
 
-template <int NHB, class Rows>
+// Cache element formats.  bf16: rows of d bf16 values.  fp8: rows of d E4M3
+// codes (OCP: sign, 4 exponent bits with bias 7, 3 mantissa bits) with one
+// fp32 scale per row, standing for code * scale [Attention variants
+// deep-dive, §7 KV Cache: fp16 -> fp8 halves the cache].  Every E4M3 value is
+// exactly a bf16, so the fp8 rows are widened to bf16 operands of the same
+// MFMAs; a key's scale multiplies its score, a value row's scale multiplies
+// its probability in the P.V product (not in the row sum).
+struct Bf16Kv {
+    static constexpr bool kFp8 = false;
+    static constexpr int kRowBytes = kD * 2;
+    struct KBuf { u32x4 r[2][4]; };                  // [block][d-step]
+    struct VBuf { u32x4 r[2][4]; };                  // [block][row]
+};
+struct Fp8Kv {
+    static constexpr bool kFp8 = true;
+    static constexpr int kRowBytes = kD;
+    struct KBuf { u32x4 r[2][2]; f32x4 s[2]; };      // 32 codes of row c at d = 32 q4 .., scales of keys 4 q4 ..
+    struct VBuf { u32x2 r[2][4]; f32x4 s[2]; };      // 8 codes of rows 4 q4 + rr at d = 8 c .., scales
+};
+
+// Eight E4M3 codes (two dwords, element e in byte e) -> eight bf16 (exact).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]), pack_bf16x2(d[0], d[1])};
+}
+
+template <int NHB, class Rows, class Fmt>
 __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, Rows rows, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ opart, float* __restrict__ lsepart, long long* __restrict__ prefix_out,
@@ -139,7 +174,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     const long long start = w * Q;
     const long long end = min(start + Q, W);
 
-    typedef u32x4 Buf[2][4];
+    typedef typename Fmt::KBuf KBuf;
+    typedef typename Fmt::VBuf VBuf;
     if (start >= end) return;
 
     // A piece: the part of one segment (b, hk) inside this wavefront's share,
@@ -173,7 +209,10 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     };
     const Piece none = {0, 0, 0, 0, 0, 0, 0, end};                  // loads nothing
 
-    // Q^T operand: lane holds Q[head hb*16 + c][32*ds + 8*q4 .. +8].  Columns
+    // Q^T operand: lane holds Q[head hb*16 + c][32*ds + 8*q4 .. +8] (fp8
+    // caches: Q[..][32*q4 + 8*ds .. +8], the order a lane's 32 contiguous K
+    // codes come in; any order of the contraction gives the same dot
+    // product, Q and K only have to agree).  Columns
     // of heads >= g repeat the group's first head (their results are never
     // written; every column of the MFMAs is independent), so the loads need
     // no branch.
@@ -184,7 +223,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
             const uint16_t* qp = q + ((size_t)p.b * Hq + p.hk * g + (hl < g ? hl : 0)) * kD;
 #pragma unroll
             for (int ds = 0; ds < 4; ++ds)
-                qf[hb][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * ds + 8 * q4));
+                qf[hb][ds] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(qp + (Fmt::kFp8 ? 32 * q4 + 8 * ds : 32 * ds + 8 * q4)));
         }
     };
 
@@ -222,23 +262,45 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     // beyond it (chunks past the end cost no memory traffic).  With a fixed
     // number of loads per chunk the wait counts stay exact, so the next
     // chunk streams in while the current one is computed.
-    auto load = [&](Buf& kr, Buf& vr, const int (&ph)[2], const Src& sr) {
+    auto load = [&](KBuf& kr, VBuf& vr, const int (&ph)[2], const Src& sr) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int t0 = sr.c0 + sr.ci * kChunk + 16 * blk;
             // (uniform; kept in scalar registers so the descriptors are too)
             const int nvalid = __builtin_amdgcn_readfirstlane(min(max(sr.p1 - t0, 0), 16));
-            const size_t off = nvalid > 0 ? rows.offset(ph[blk], sr.b, sr.hk, t0) : 0;
-            const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows.kbase + off, (uint32_t)nvalid * kD * 2);
-            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows.vbase + off, (uint32_t)nvalid * kD * 2);
+            const size_t row = nvalid > 0 ? rows.row(ph[blk], sr.b, sr.hk, t0) : 0;
+            const __amdgpu_buffer_rsrc_t krs =
+                make_rsrc(rows.kbase + row * Fmt::kRowBytes, (uint32_t)nvalid * Fmt::kRowBytes);
+            const __amdgpu_buffer_rsrc_t vrs =
+                make_rsrc(rows.vbase + row * Fmt::kRowBytes, (uint32_t)nvalid * Fmt::kRowBytes);
+            if constexpr (!Fmt::kFp8) {
 #pragma unroll
-            for (int ds = 0; ds < 4; ++ds)
-                kr[blk][ds] = __builtin_amdgcn_raw_buffer_load_b128(
-                    krs, (uint32_t)(c * kD + 32 * ds + 8 * q4) * 2, 0, kStreamAux);
+                for (int ds = 0; ds < 4; ++ds)
+                    kr.r[blk][ds] = __builtin_amdgcn_raw_buffer_load_b128(
+                        krs, (uint32_t)(c * kD + 32 * ds + 8 * q4) * 2, 0, kStreamAux);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                vr[blk][rr] = __builtin_amdgcn_raw_buffer_load_b128(
-                    vrs, (uint32_t)((4 * q4 + rr) * kD + 8 * c) * 2, 0, kStreamAux);
+                for (int rr = 0; rr < 4; ++rr)
+                    vr.r[blk][rr] = __builtin_amdgcn_raw_buffer_load_b128(
+                        vrs, (uint32_t)((4 * q4 + rr) * kD + 8 * c) * 2, 0, kStreamAux);
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    kr.r[blk][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                        krs, (uint32_t)(c * kD + 32 * q4 + 16 * h), 0, kStreamAux);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    vr.r[blk][rr] = __builtin_amdgcn_raw_buffer_load_b64(
+                        vrs, (uint32_t)((4 * q4 + rr) * kD + 8 * c), 0, kStreamAux);
+                // The scales of all 16 rows of a block with any valid row are
+                // read (a block's rows all exist in memory); those of rows past
+                // the valid ones are never used: their scores are masked and
+                // their probabilities are zero.  An empty block reads nothing.
+                const uint32_t sbytes = nvalid > 0 ? 64u : 0u;
+                const __amdgpu_buffer_rsrc_t kss = make_rsrc(rows.kscale + row, sbytes);
+                const __amdgpu_buffer_rsrc_t vss = make_rsrc(rows.vscale + row, sbytes);
+                kr.s[blk] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(kss, 16u * q4, 0, 0));
+                vr.s[blk] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vss, 16u * q4, 0, 0));
+            }
         }
     };
 
@@ -246,8 +308,24 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     float ref[NHB], lsum[NHB];
     f32x4 oacc[NHB][8];
 
-    auto process = [&](const Buf& kr, const Buf& vr, const Piece& cur, int ci) {
+    auto process = [&](const KBuf& kr, const VBuf& vr, const Piece& cur, int ci) {
         bf16x4 pf[NHB][2];
+        // bf16 operands of the chunk: K for each block and d-step, V rows
+        // (fp8 codes widened once, for all head blocks).
+        u32x4 kop[2][4], vrow[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                if constexpr (!Fmt::kFp8) {
+                    kop[blk][x] = kr.r[blk][x];
+                    vrow[blk][x] = vr.r[blk][x];
+                } else {
+                    const u32x4 w = kr.r[blk][x >> 1];
+                    kop[blk][x] = (x & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+                    vrow[blk][x] = fp8x8_to_bf16x8(vr.r[blk][x][0], vr.r[blk][x][1]);
+                }
+            }
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             float s[2][4];
@@ -256,12 +334,14 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                 f32x4 acc = f32x4{};
 #pragma unroll
                 for (int ds = 0; ds < 4; ++ds)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[blk][ds]),
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[blk][ds]),
                                                                    qf[hb][ds], acc, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = cur.c0 + ci * kChunk + 16 * blk + 4 * q4 + r;
-                    s[blk][r] = (key >= cur.p0 && key < cur.p1) ? acc[r] : -INFINITY;
+                    float sc = acc[r];
+                    if constexpr (Fmt::kFp8) sc *= kr.s[blk][r];
+                    s[blk][r] = (key >= cur.p0 && key < cur.p1) ? sc : -INFINITY;
                 }
             }
             float tmax = s[0][0];
@@ -287,6 +367,9 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                 for (int r = 0; r < 4; ++r) {
                     p[r] = exp2_fast(fmaf(s[blk][r], scale_log2, -ref[hb]));
                     lsum[hb] += p[r];
+                    // fp8: the value row's scale (a masked row's p is 0 and its
+                    // scale is never read as a number)
+                    if constexpr (Fmt::kFp8) p[r] = p[r] > 0.f ? p[r] * vr.s[blk][r] : 0.f;
                 }
                 u32x2 x;
                 x.x = pack_bf16x2(p[0], p[1]);
@@ -302,11 +385,11 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                 const int dw = j >> 1;
                 u32x2 a;
                 if (j & 1) {
-                    a.x = pack_hi16(vr[blk][0][dw], vr[blk][1][dw]);
-                    a.y = pack_hi16(vr[blk][2][dw], vr[blk][3][dw]);
+                    a.x = pack_hi16(vrow[blk][0][dw], vrow[blk][1][dw]);
+                    a.y = pack_hi16(vrow[blk][2][dw], vrow[blk][3][dw]);
                 } else {
-                    a.x = pack_lo16(vr[blk][0][dw], vr[blk][1][dw]);
-                    a.y = pack_lo16(vr[blk][2][dw], vr[blk][3][dw]);
+                    a.x = pack_lo16(vrow[blk][0][dw], vrow[blk][1][dw]);
+                    a.y = pack_lo16(vrow[blk][2][dw], vrow[blk][3][dw]);
                 }
                 const bf16x4 av = __builtin_bit_cast(bf16x4, a);
 #pragma unroll
@@ -342,7 +425,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
 
     // Two chunk buffers (chunk x of a piece in buffer x % 2) with their table
     // entries.
-    Buf ka, va, kb, vb;
+    KBuf ka, kb;
+    VBuf va, vb;
     int pha[2], phb[2];
     auto pair = [&](const Piece& cur, const Piece& nxt, int ci, bool last) {
         lookup(pha, src_of(cur, nxt, ci + 2));
@@ -460,7 +544,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
     }
 }
 
-template <int NHB, class Rows>
+template <int NHB, class Fmt, class Rows>
 hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -474,7 +558,7 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
     long long* prefix = reinterpret_cast<long long*>(base + ws.prefix);
     const int P = decode_max_partials(a.max_seq_len);
     const int g = a.Hq / a.Hkv;
-    hipLaunchKernelGGL((decode_split_kernel<NHB, Rows>), dim3(nwg), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<NHB, Rows, Fmt>), dim3(nwg), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(a.q), rows, a.block_table, a.seq_lens, opart, lsepart, prefix, a.B,
                        a.Hq, g, P,
                        a.scale * kLog2e);
@@ -485,19 +569,24 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
     return hipGetLastError();
 }
 
-template <class Rows>
+template <class Fmt, class Rows>
 hipError_t launch_rows(const DecodeArgs& a, const Rows& rows, hipStream_t stream) {
-    return a.Hq / a.Hkv <= 16 ? launch_both<1>(a, rows, stream) : launch_both<2>(a, rows, stream);
+    return a.Hq / a.Hkv <= 16 ? launch_both<1, Fmt>(a, rows, stream) : launch_both<2, Fmt>(a, rows, stream);
+}
+
+template <class Fmt>
+hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream) {
+    const char* kc = static_cast<const char*>(a.k_cache);
+    const char* vc = static_cast<const char*>(a.v_cache);
+    if (a.block_table)
+        return launch_rows<Fmt>(a, PagedRows{kc, vc, a.k_scale, a.v_scale, a.Hkv, a.max_blocks_per_seq}, stream);
+    return launch_rows<Fmt>(a, ContiguousRows{kc, vc, a.k_scale, a.v_scale, a.Hkv, a.max_seq_len}, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-    const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-    if (a.block_table)
-        return launch_rows(a, PagedRows{kc, vc, a.Hkv, a.max_blocks_per_seq}, stream);
-    return launch_rows(a, ContiguousRows{kc, vc, a.Hkv, a.max_seq_len}, stream);
-}
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_fmt<Bf16Kv>(a, stream); }
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) { return launch_fmt<Fp8Kv>(a, stream); }
 
 }  // namespace gqa

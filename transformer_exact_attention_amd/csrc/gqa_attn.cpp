@@ -122,6 +122,22 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+int attn_decode_fp8_fwd(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, void* o, const int32_t* seq_lens, const int32_t* block_table, int B,
+                        int Hq, int Hkv, int d, int max_seq_len, int block_size, int max_blocks_per_seq, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!k_scale || !v_scale) return GQA_ERR_INVALID_ARG;
+    const int st = decode_check(q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
+                                block_size, max_blocks_per_seq, scale, GQA_BF16, workspace, workspace_bytes);
+    if (st != GQA_OK) return st;
+    // a contiguous cache's scale rows are read 16 at a time from block starts
+    if (!block_table && max_seq_len % GQA_PAGE_BLOCK_SIZE != 0) return GQA_ERR_UNSUPPORTED;
+    gqa::DecodeArgs a{q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
+                      block_table ? max_blocks_per_seq : 0, scale, workspace, k_scale, v_scale};
+    const hipError_t e = gqa::launch_decode_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 int attn_decode_validate(const int32_t* seq_lens, const int32_t* block_table, int B, int max_seq_len,
                          int block_size, int max_blocks_per_seq, int num_physical_blocks, void* stream) {
     if (!seq_lens || B <= 0 || max_seq_len < 0) return GQA_ERR_INVALID_ARG;

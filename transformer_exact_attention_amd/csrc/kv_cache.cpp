@@ -266,9 +266,34 @@ int attn_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const 
     int row_bytes = 0;
     const int st = checked_rows(n, Hkv, d, dtype, row_bytes);
     if (st != GQA_OK) return st;
-    if ((int64_t)n * Hkv * kBlock >= ((int64_t)1 << 31)) return GQA_ERR_INVALID_ARG;
+    if ((int64_t)n * Hkv * kBlock * (row_bytes / 16) >= ((int64_t)1 << 31)) return GQA_ERR_INVALID_ARG;
     if (n == 0) return GQA_OK;
     gqa::KvCopyArgs a{k_cache, v_cache, src, dst, n, num_blocks, Hkv, row_bytes};
+    return gqa::launch_kv_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int attn_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const void* k_new,
+                       const void* v_new, const int32_t* slots, int n_tokens, int num_blocks, int Hkv, int d,
+                       void* stream) {
+    if (!k_cache || !v_cache || !k_scale || !v_scale || !k_new || !v_new || !slots || num_blocks <= 0)
+        return GQA_ERR_INVALID_ARG;
+    if (n_tokens < 0 || Hkv <= 0 || d <= 0) return GQA_ERR_INVALID_ARG;
+    if (d != 128) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)n_tokens * Hkv * kBlock >= ((int64_t)1 << 31) || (int64_t)num_blocks * kBlock >= ((int64_t)1 << 31))
+        return GQA_ERR_INVALID_ARG;
+    if (n_tokens == 0) return GQA_OK;
+    gqa::KvAppendArgs a{k_cache, v_cache, k_new, v_new, slots, n_tokens, num_blocks, Hkv, d, k_scale, v_scale};
+    return gqa::launch_kv_append_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int attn_kv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const int32_t* src,
+                            const int32_t* dst, int n, int num_blocks, int Hkv, int d, void* stream) {
+    if (!k_cache || !v_cache || !k_scale || !v_scale || !src || !dst || num_blocks <= 0) return GQA_ERR_INVALID_ARG;
+    if (n < 0 || Hkv <= 0 || d <= 0) return GQA_ERR_INVALID_ARG;
+    if (d != 128) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)n * Hkv * kBlock * (d / 16) >= ((int64_t)1 << 31)) return GQA_ERR_INVALID_ARG;
+    if (n == 0) return GQA_OK;
+    gqa::KvCopyArgs a{k_cache, v_cache, src, dst, n, num_blocks, Hkv, d, k_scale, v_scale};
     return gqa::launch_kv_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 

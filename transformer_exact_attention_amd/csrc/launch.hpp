@@ -29,6 +29,8 @@ struct DecodeArgs {
     int max_blocks_per_seq;
     float scale;
     void* workspace;
+    const float* k_scale = nullptr;   // fp8 caches: per-row scales, same row numbering as the cache
+    const float* v_scale = nullptr;
 };
 
 // Decode work partition.  The flattened space of (sequence, K/V head, token)
@@ -67,6 +69,8 @@ inline size_t decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
 
 // Paged KV cache: new tokens [n_tokens, Hkv, d] to their slots, and whole
 // block copies; rows are row_bytes = d * element size bytes (16 | row_bytes).
+// fp8 caches add per-row fp32 scales [num_blocks, Hkv, 16] (k_scale,
+// v_scale; null for bf16/fp32 caches).
 struct KvAppendArgs {
     void* k_cache;
     void* v_cache;
@@ -74,6 +78,8 @@ struct KvAppendArgs {
     const void* v_new;
     const int32_t* slots;
     int n_tokens, num_blocks, Hkv, row_bytes;
+    float* k_scale = nullptr;
+    float* v_scale = nullptr;
 };
 struct KvCopyArgs {
     void* k_cache;
@@ -81,12 +87,16 @@ struct KvCopyArgs {
     const int32_t* src;
     const int32_t* dst;
     int n, num_blocks, Hkv, row_bytes;
+    float* k_scale = nullptr;
+    float* v_scale = nullptr;
 };
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_copy_blocks(const KvCopyArgs& a, hipStream_t stream);
+hipError_t launch_kv_append_fp8(const KvAppendArgs& a, hipStream_t stream);
 
 }  // namespace gqa

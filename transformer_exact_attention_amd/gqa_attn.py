@@ -27,7 +27,8 @@ EXPORTS = ("gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
            "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_decode_validate",
            "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks", "gqa_kv_seq_new",
            "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len", "gqa_kv_reserve", "gqa_kv_block_table",
-           "attn_kv_append", "attn_kv_copy_blocks")
+           "attn_kv_append", "attn_kv_copy_blocks", "attn_decode_fp8_fwd", "attn_kv_append_fp8",
+           "attn_kv_copy_blocks_fp8")
 
 _lib = None
 
@@ -85,6 +86,12 @@ def load_library(path: str = LIB_PATH):
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 5 + [vp]
     lib.attn_kv_copy_blocks.restype = c_int
     lib.attn_kv_copy_blocks.argtypes = [vp, vp, vp, vp] + [c_int] * 5 + [vp]
+    lib.attn_decode_fp8_fwd.restype = c_int
+    lib.attn_decode_fp8_fwd.argtypes = [vp] * 8 + [c_int] * 7 + [c_float, vp, c_size, vp]
+    lib.attn_kv_append_fp8.restype = c_int
+    lib.attn_kv_append_fp8.argtypes = [vp] * 7 + [c_int] * 4 + [vp]
+    lib.attn_kv_copy_blocks_fp8.restype = c_int
+    lib.attn_kv_copy_blocks_fp8.argtypes = [vp] * 6 + [c_int] * 4 + [vp]
     _lib = lib
     return lib
 
@@ -364,3 +371,117 @@ def attn_kv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch
     code = _dtype_code(k_cache, v_cache)
     _raise(lib.attn_kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src.data_ptr(), dst.data_ptr(), n,
                                    num_blocks, Hkv, d, code, _stream(stream)), "attn_kv_copy_blocks")
+
+
+# ---- fp8 KV caches (E4M3 codes + one fp32 scale per row) -------------------
+
+def _fp8_pages(k_cache, v_cache, k_scale, v_scale):
+    num_blocks, Hkv, d = _page_dims(k_cache, v_cache)
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches hold uint8 E4M3 codes")
+    for sc in (k_scale, v_scale):
+        if sc.dtype != torch.float32 or tuple(sc.shape) != (num_blocks, Hkv, PAGE_BLOCK_SIZE):
+            raise ValueError("fp8 scales must be float32 [num_blocks, Hkv, 16]")
+    return num_blocks, Hkv, d
+
+
+def attn_kv_append_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                       k_new: torch.Tensor, v_new: torch.Tensor, slots: torch.Tensor, stream=None):
+    """Quantise bf16 tokens [n, Hkv, d] into fp8 pages and their row scales at slots."""
+    lib = load_library()
+    num_blocks, Hkv, d = _fp8_pages(k_cache, v_cache, k_scale, v_scale)
+    n = k_new.shape[0]
+    if k_new.dim() != 3 or tuple(k_new.shape) != (n, Hkv, d) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new and v_new must both be [n_tokens, Hkv, d]")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("new tokens are bfloat16")
+    if slots.dtype != torch.int32 or tuple(slots.shape) != (n,):
+        raise ValueError("slots must be int32 [n_tokens]")
+    if n == 0:
+        return
+    _dev(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slots)
+    _raise(lib.attn_kv_append_fp8(k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                                  k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(), n, num_blocks, Hkv, d,
+                                  _stream(stream)), "attn_kv_append_fp8")
+
+
+def attn_kv_copy_blocks_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                            v_scale: torch.Tensor, src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Copy whole fp8 blocks src[i] -> dst[i] with their row scales."""
+    lib = load_library()
+    num_blocks, Hkv, d = _fp8_pages(k_cache, v_cache, k_scale, v_scale)
+    n = src.shape[0]
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.dim() != 1 or tuple(dst.shape) != (n,):
+        raise ValueError("src and dst must be int32 [n]")
+    if n == 0:
+        return
+    _dev(k_cache, v_cache, k_scale, v_scale, src, dst)
+    _raise(lib.attn_kv_copy_blocks_fp8(k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                                       v_scale.data_ptr(), src.data_ptr(), dst.data_ptr(), n, num_blocks, Hkv, d,
+                                       _stream(stream)), "attn_kv_copy_blocks_fp8")
+
+
+def attn_decode_fp8_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                        v_scale: torch.Tensor, seq_lens: torch.Tensor, o: Optional[torch.Tensor] = None, *,
+                        block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None,
+                        scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """attn_decode_fwd over an fp8 cache: uint8 codes laid out like the bf16
+    caches, fp32 scales [B,Hkv,S_max] (contiguous) or [num_blocks,Hkv,16]
+    (paged); q and o bf16."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q must be [B,Hq,d]; k_cache and v_cache 4-D and equal in shape")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches hold uint8 E4M3 codes")
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[3] != d:
+        raise ValueError("head dim mismatch")
+    if tuple(k_scale.shape) != tuple(k_cache.shape[:3]) or tuple(v_scale.shape) != tuple(k_scale.shape):
+        raise ValueError("scales must have the cache's shape without d")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise ValueError("scales are float32")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    tensors = [q, k_cache, v_cache, k_scale, v_scale, seq_lens]
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[2] != PAGE_BLOCK_SIZE:
+            raise ValueError("paged caches hold 16 tokens per block")
+        max_blocks = block_table.shape[1]
+        if max_seq_len is None:
+            max_seq_len = max_blocks * PAGE_BLOCK_SIZE
+        tensors.append(block_table)
+        bt_ptr = block_table.data_ptr()
+        block_size = PAGE_BLOCK_SIZE
+    else:
+        if k_cache.shape[0] != B:
+            raise ValueError("contiguous cache must be [B,Hkv,S_max,d]")
+        max_blocks = 0
+        block_size = 0
+        if max_seq_len is None:
+            max_seq_len = k_cache.shape[2]
+        if max_seq_len != k_cache.shape[2]:
+            raise ValueError("contiguous cache: max_seq_len must equal S_max")
+        bt_ptr = None
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q is bfloat16")
+    if o is None:
+        o = torch.empty_like(q)
+    if tuple(o.shape) != tuple(q.shape) or o.dtype != torch.bfloat16:
+        raise ValueError("o must be bfloat16 with q's shape")
+    tensors.append(o)
+    _dev(*tensors)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, d, max_seq_len, q.device)
+    _dev(workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_decode_fp8_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                                 v_scale.data_ptr(), o.data_ptr(), seq_lens.data_ptr(), bt_ptr, B, Hq, Hkv, d,
+                                 int(max_seq_len), block_size, max_blocks, float(scale), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise(st, "attn_decode_fp8_fwd")
+    return o
