@@ -50,8 +50,9 @@ def parse():
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload separately (one JSON line each) instead of the step")
-    ap.add_argument("--sweep-kinds", default="prefill,decode,kv",
-                    help="comma list of the sweep's parts: prefill, decode, kv (paged KV-cache writes)")
+    ap.add_argument("--sweep-kinds", default="prefill,decode,kv,fp8",
+                    help="comma list of the sweep's parts: prefill, decode, kv (paged KV-cache writes), "
+                         "fp8 (decode over fp8 caches)")
     return ap.parse_args()
 
 
@@ -192,6 +193,70 @@ def sweep(args):
         torch.cuda.empty_cache()
     if "kv" in kinds:
         sweep_kv(args, timed, dev, stream)
+    if "fp8" in kinds:
+        sweep_fp8(args, dev, stream, flush)
+
+
+def sweep_fp8(args, dev, stream, flush):
+    """Decode over fp8 caches (E4M3 codes + one fp32 scale per row) built from
+    each decode workload's bf16 cache by the library's quantising append.
+    Bytes = codes plus scales of every cached row, read once."""
+    import torch
+    from transformer_exact_attention_amd import gqa_attn
+    from transformer_exact_attention_amd import workloads as W
+    for w in (W.CFG4, W.cfg5(32), W.cfg5(8), W.cfg5(1)):
+        log(f"sweep fp8 {w.name}")
+        di = W.decode_inputs(w)
+
+        def to_fp8(bits):
+            # rows [..., Hkv, S, d] -> tokens [rows/Hkv.., Hkv, d] in slot order, quantised in place of the bf16
+            t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+            shape = t.shape
+            if w.paged:                                  # [nb, Hkv, 16, d]: slot s = block * 16 + offset
+                toks = t.permute(0, 2, 1, 3).contiguous().reshape(-1, shape[1], shape[3])
+                hkv = shape[1]
+            else:                                        # [B, Hkv, S, d]: one head per "block row" (Hkv = 1)
+                toks = t.reshape(-1, 1, shape[3])
+                hkv = 1
+            n = toks.shape[0]
+            codes = torch.empty((n // 16, hkv, 16, shape[3]), dtype=torch.uint8, device=dev)
+            scales = torch.empty((n // 16, hkv, 16), dtype=torch.float32, device=dev)
+            return toks, codes, scales, shape
+        kt, kq, ksc, shape = to_fp8(di.k_cache)
+        vt, vq, vsc, _ = to_fp8(di.v_cache)
+        slots = torch.arange(kt.shape[0], dtype=torch.int32, device=dev)
+        gqa_attn.attn_kv_append_fp8(kq, vq, ksc, vsc, kt, vt, slots, stream=stream)
+        del kt, vt, slots
+        kq, vq = kq.reshape(shape), vq.reshape(shape)
+        ksc, vsc = ksc.reshape(shape[:3]), vsc.reshape(shape[:3])
+        q = torch.from_numpy(np.ascontiguousarray(di.q).view(np.int16)).view(torch.bfloat16).to(dev)
+        lens = torch.from_numpy(di.seq_lens).to(dev)
+        bt = torch.from_numpy(di.block_table).to(dev) if w.paged else None
+        o = torch.empty_like(q)
+        ws = gqa_attn.decode_workspace(w.B, w.Hq, w.d, di.max_seq_len, dev)
+        rows = int(di.seq_lens.sum()) * w.Hkv * 2
+        nbytes = rows * (w.d + 4)
+        msl = w.max_blocks * W.BLOCK_SIZE if w.paged else None
+        del di
+        ev = []
+        for it in range(args.warmup + args.steps):
+            flush.fill_(1)                      # evict the 256 MB Infinity Cache before every call
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            gqa_attn.attn_decode_fp8_fwd(q, kq, vq, ksc, vsc, lens, o, block_table=bt, max_seq_len=msl,
+                                         scale=w.scale_value, workspace=ws, stream=stream)
+            b.record(stream)
+            if it >= args.warmup:
+                ev.append((a, b))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        gbs = nbytes / float(np.mean(t)) / 1e9
+        print(json.dumps({"workload": w.name + "_fp8", "kind": "decode_fp8", "kv_bytes": nbytes,
+                          "avg_us": round(float(np.mean(t)) * 1e6, 2), "min_us": round(float(np.min(t)) * 1e6, 2),
+                          "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                          "tokens_per_s": round(w.B / float(np.mean(t)), 1)}), flush=True)
+        del q, kq, vq, ksc, vsc, lens, bt, o, ws
+        torch.cuda.empty_cache()
 
 
 def sweep_kv(args, timed, dev, stream):

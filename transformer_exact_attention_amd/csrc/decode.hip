@@ -118,13 +118,13 @@ struct Fp8Kv {
     struct VBuf { u32x2 r[2][4]; f32x4 s[2]; };      // 8 codes of rows 4 q4 + rr at d = 8 c .., scales
 };
 
-// Eight E4M3 codes (two dwords, element e in byte e) -> eight bf16 (exact).
+// Eight E4M3 codes (two dwords, element e in byte e) -> eight bf16, exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: two codes per instruction).
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]), pack_bf16x2(d[0], d[1])};
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
 }
 
 template <int NHB, class Rows, class Fmt>
