@@ -6,5 +6,5 @@ leg may import this package.
 from .core import (  # noqa: F401
     attention, attention_head, attention_rows, bf16_bits_to_f64, causal_visible,
     combine_partials, decode_contiguous, decode_paged, default_scale, flash_forward_replay,
-    kv_cache_bytes, kv_head_index, paged_logical_rows, split_partials, to_f64,
+    kv_cache_bytes, kv_head_index, paged_logical_rows, split_partials, to_f64, window_visible,
 )

@@ -89,13 +89,27 @@ def causal_visible(rows: np.ndarray, Sq: int, Sk: int) -> np.ndarray:
     return j <= (np.asarray(rows)[:, None] + (Sk - Sq))
 
 
+def window_visible(rows: np.ndarray, Sq: int, Sk: int, window: int) -> np.ndarray:
+    """Boolean [len(rows), Sk]: sliding window of ``window`` keys ending at the
+    causal diagonal, key j visible to row i iff i + Sk - Sq - window < j <= i + Sk - Sq.
+
+    The pages only name sliding-window attention for long sequences
+    [Attention variants deep-dive, §8 Q4]; the reading: each query sees its
+    last ``window`` keys (itself included), causal.
+    """
+    j = np.arange(Sk)[None, :]
+    last = np.asarray(rows)[:, None] + (Sk - Sq)
+    return (j <= last) & (j > last - window)
+
+
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   causal: bool = False, rows=None):
+                   causal: bool = False, rows=None, window=None):
     """Attention of one query head over one K/V head, in float64.
 
     q [Sq, d], k [Sk, d], v [Sk, d].  ``rows`` selects query rows (default:
-    all).  Returns (o [R, d], lse [R], p [R, Sk]): the output, the natural-log
-    normaliser m + ln(l), and the probability matrix.
+    all).  ``window`` (>= 1) restricts each row to its last ``window`` keys
+    and implies causal.  Returns (o [R, d], lse [R], p [R, Sk]): the output,
+    the natural-log normaliser m + ln(l), and the probability matrix.
     Rows with no visible key give o = 0 and lse = -inf.
     """
     q = np.asarray(q, np.float64)
@@ -107,7 +121,9 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     if Sk == 0 or R == 0:
         return np.zeros((R, dv)), np.full(R, NEG_INF), np.zeros((R, Sk))
     s = (q[rows] @ k.T) * scale                       # scores, [R, Sk]
-    if causal:
+    if window is not None:
+        s = np.where(window_visible(rows, Sq, Sk, window), s, NEG_INF)
+    elif causal:
         s = np.where(causal_visible(rows, Sq, Sk), s, NEG_INF)
     m = s.max(axis=1, keepdims=True)                  # row max (stable softmax)
     empty = ~np.isfinite(m[:, 0])
@@ -123,7 +139,7 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return o, lse, p
 
 
-def attention(q, k, v, scale=None, causal=False, return_lse=False):
+def attention(q, k, v, scale=None, causal=False, return_lse=False, window=None):
     """Grouped-query attention, q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] -> o [B,Hq,Sq,d].
 
     MHA when Hkv == Hq, MQA when Hkv == 1 [Attention variants deep-dive, §4 GQA].
@@ -135,7 +151,7 @@ def attention(q, k, v, scale=None, causal=False, return_lse=False):
     Bk, Hkv, Sk, dk = k.shape
     if Bk != B or dk != d or v.shape[:3] != k.shape[:3]:
         raise ValueError("shape mismatch")
-    if causal and Sq > Sk:
+    if (causal or window is not None) and Sq > Sk:
         raise ValueError("causal attention needs Sq <= Sk")
     if scale is None:
         scale = default_scale(d)
@@ -144,11 +160,11 @@ def attention(q, k, v, scale=None, causal=False, return_lse=False):
     for b in range(B):
         for hq in range(Hq):
             hk = kv_head_index(hq, Hq, Hkv)
-            o[b, hq], lse[b, hq], _ = attention_head(q[b, hq], k[b, hk], v[b, hk], scale, causal)
+            o[b, hq], lse[b, hq], _ = attention_head(q[b, hq], k[b, hk], v[b, hk], scale, causal, window=window)
     return (o, lse) if return_lse else o
 
 
-def attention_rows(q, k, v, b: int, hq: int, rows, scale=None, causal=False):
+def attention_rows(q, k, v, b: int, hq: int, rows, scale=None, causal=False, window=None):
     """Selected output rows of query head ``hq`` in batch ``b`` (for sampled checks)."""
     B, Hq, Sq, d = q.shape
     Hkv = k.shape[1]
@@ -156,21 +172,22 @@ def attention_rows(q, k, v, b: int, hq: int, rows, scale=None, causal=False):
         scale = default_scale(d)
     hk = kv_head_index(hq, Hq, Hkv)
     o, lse, _ = attention_head(np.asarray(q[b, hq], np.float64), np.asarray(k[b, hk], np.float64),
-                               np.asarray(v[b, hk], np.float64), scale, causal, rows)
+                               np.asarray(v[b, hk], np.float64), scale, causal, rows, window)
     return o, lse
 
 
 # ----------------------------------------------------------------------------
 # decode over a KV cache
 # ----------------------------------------------------------------------------
-def decode_contiguous(q, k_cache, v_cache, seq_lens, scale=None, heads=None, return_lse=False):
+def decode_contiguous(q, k_cache, v_cache, seq_lens, scale=None, heads=None, return_lse=False, window=None):
     """One new query token per sequence over a contiguous cache.
 
     q [B,Hq,d]; k_cache/v_cache [B,Hkv,S_max,d]; seq_lens [B].  Query b attends
     cached keys [0, L_b) with no mask [Attention variants deep-dive, §7 KV
     Cache: each step only the new token's Q against the cached K/V].
     ``heads`` optionally restricts the work to a list of (b, hq) pairs (others
-    are left zero).
+    are left zero).  ``window``: the query attends only keys
+    [max(0, L_b - window), L_b) (its last ``window`` tokens).
     """
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
@@ -181,9 +198,10 @@ def decode_contiguous(q, k_cache, v_cache, seq_lens, scale=None, heads=None, ret
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     for b, hq in pairs:
         L = int(seq_lens[b])
+        lo = max(0, L - window) if window is not None else 0
         hk = kv_head_index(hq, Hq, Hkv)
-        kb = np.asarray(k_cache[b, hk, :L], np.float64)
-        vb = np.asarray(v_cache[b, hk, :L], np.float64)
+        kb = np.asarray(k_cache[b, hk, lo:L], np.float64)
+        vb = np.asarray(v_cache[b, hk, lo:L], np.float64)
         ob, lb, _ = attention_head(np.asarray(q[b, hq], np.float64)[None, :], kb, vb, scale)
         o[b, hq], lse[b, hq] = ob[0], lb[0]
     return (o, lse) if return_lse else o
@@ -204,8 +222,9 @@ def paged_logical_rows(pages, block_table_row, hk: int, L: int, block_size: int 
 
 
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, block_size=16,
-                 heads=None, return_lse=False):
-    """Decode over a paged cache: gather the logical K/V rows, then the definition."""
+                 heads=None, return_lse=False, window=None):
+    """Decode over a paged cache: gather the logical K/V rows, then the definition
+    (``window`` as in decode_contiguous)."""
     B, Hq, d = q.shape
     Hkv = k_pages.shape[1]
     if scale is None:
@@ -223,7 +242,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, block_s
                 np.asarray(paged_logical_rows(k_pages, block_table[b], hk, L, block_size), np.float64),
                 np.asarray(paged_logical_rows(v_pages, block_table[b], hk, L, block_size), np.float64))
         kb, vb = cache[(b, hk)]
-        ob, lb, _ = attention_head(np.asarray(q[b, hq], np.float64)[None, :], kb, vb, scale)
+        lo = max(0, L - window) if window is not None else 0
+        ob, lb, _ = attention_head(np.asarray(q[b, hq], np.float64)[None, :], kb[lo:], vb[lo:], scale)
         o[b, hq], lse[b, hq] = ob[0], lb[0]
     return (o, lse) if return_lse else o
 
