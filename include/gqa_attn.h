@@ -82,6 +82,20 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o,
                      float scale, int causal, int dtype, void* stream);
 
 /*
+ * Sliding-window attention forward: attn_prefill_fwd with causal != 0 where
+ * each query additionally sees only its last `window` keys -- key j is
+ * visible to query row i iff i + (Sk - Sq) - window < j <= i + (Sk - Sq).
+ * The pages name sliding-window attention for long sequences [Attention
+ * variants deep-dive, §8 Q4] and fix nothing else; this is the plain
+ * reading.  Tiles wholly before a query block's window are neither read nor
+ * computed.  window >= 1 (window >= Sk is plain causal attention); otherwise
+ * as attn_prefill_fwd, with GQA_ERR_INVALID_ARG for window <= 0.
+ */
+int attn_prefill_window_fwd(const void* q, const void* k, const void* v, void* o,
+                            int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                            float scale, int window, int dtype, void* stream);
+
+/*
  * Bytes of device workspace attn_decode_fwd needs for these sizes (an upper
  * bound valid for every Hkv dividing Hq).  0 on invalid sizes.
  */
@@ -124,6 +138,21 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
                     int block_size, int max_blocks_per_seq,
                     float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sliding-window decode: attn_decode_fwd where query b attends only its
+ * sequence's last `window` cached keys, [max(0, L_b - window), L_b) (the
+ * reading of [Attention variants deep-dive, §8 Q4], as for
+ * attn_prefill_window_fwd).  Keys before the window are never read; the
+ * work split covers min(L_b, window) tokens per sequence.  window >= 1;
+ * otherwise as attn_decode_fwd, with GQA_ERR_INVALID_ARG for window <= 0.
+ */
+int attn_decode_window_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
+                           const int32_t* seq_lens, const int32_t* block_table,
+                           int B, int Hq, int Hkv, int d, int max_seq_len,
+                           int block_size, int max_blocks_per_seq,
+                           float scale, int window, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode over an fp8 KV cache [Attention variants deep-dive, §7 KV Cache:

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                             "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks",
                             "gqa_kv_seq_new", "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len",
                             "gqa_kv_reserve", "gqa_kv_block_table", "attn_kv_append", "attn_kv_copy_blocks",
-                            "attn_decode_fp8_fwd", "attn_kv_append_fp8", "attn_kv_copy_blocks_fp8"])
+                            "attn_decode_fp8_fwd", "attn_kv_append_fp8", "attn_kv_copy_blocks_fp8",
+                            "attn_prefill_window_fwd", "attn_decode_window_fwd"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -147,3 +148,23 @@ def decode_fp8(lib, **kw):
 ])
 def test_decode_fp8_rejects_on_host(lib, kw, status):
     assert decode_fp8(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(window=0), 1), (dict(window=-3), 1), (dict(Sq=17, Sk=16), 1),
+                                       (dict(q=None), 1), (dict(d=96), 2)])
+def test_prefill_window_rejects_on_host(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=4, Hkv=2, Sq=16, Sk=16, d=64, scale=0.125, window=8, dtype=1)
+    a.update(kw)
+    assert lib.attn_prefill_window_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                       a["d"], a["scale"], a["window"], a["dtype"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(window=0), 1), (dict(lens=None), 1), (dict(dtype=0), 2),
+                                       (dict(ws=None), 3)])
+def test_decode_window_rejects_on_host(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, table=None, B=2, Hq=8, Hkv=2, d=128, max_seq_len=64,
+             block_size=0, max_blocks=0, scale=0.1, window=16, dtype=1, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.attn_decode_window_fwd(a["q"], a["k"], a["v"], a["o"], a["lens"], a["table"], a["B"], a["Hq"],
+                                      a["Hkv"], a["d"], a["max_seq_len"], a["block_size"], a["max_blocks"],
+                                      a["scale"], a["window"], a["dtype"], a["ws"], a["ws_bytes"], None) == status

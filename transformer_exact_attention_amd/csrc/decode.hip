@@ -131,20 +131,22 @@ template <int NHB, class Rows, class Fmt>
 __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, Rows rows, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ opart, float* __restrict__ lsepart, long long* __restrict__ prefix_out,
-    int B, int Hq, int g, int P, float scale_log2) {
+    int B, int Hq, int g, int P, float scale_log2, int window) {
     __shared__ long long pre[kDecodeMaxBatch + 1];
     __shared__ long long part[kThreads];
 
     const int tid = threadIdx.x;
     const int Hkv = Hq / g;
 
-    // Token prefix sums over sequences: pre[b] = sum of L_b' for b' < b.
+    // Token prefix sums over sequences: pre[b] = sum of L_b' for b' < b,
+    // where a sliding window (window > 0) keeps only a sequence's last
+    // `window` tokens: its segment is tokens [L - min(L, window), L).
     {
         const int per = (B + kThreads - 1) / kThreads;
         const int lo = min(B, tid * per), hi = min(B, lo + per);
         long long acc = 0;
         for (int i = lo; i < hi; ++i) {
-            acc += seq_lens[i];
+            acc += window > 0 ? min(seq_lens[i], window) : seq_lens[i];
             pre[i + 1] = acc;
         }
         part[tid] = acc;
@@ -199,12 +201,15 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
         const long long seg0 = uniform64(pre[p.b] * Hkv);
         p.hk = __builtin_amdgcn_readfirstlane((int)((pos - seg0) / L));
         const long long S = seg0 + (long long)p.hk * L;               // segment start
-        p.p0 = __builtin_amdgcn_readfirstlane((int)(pos - S));
-        p.p1 = __builtin_amdgcn_readfirstlane((int)(min(end, S + L) - S));
+        // first cached token of the segment (window: the sequence's last L tokens)
+        const int t_first = window > 0 ? __builtin_amdgcn_readfirstlane(seq_lens[p.b]) - L : 0;
+        const int p1 = __builtin_amdgcn_readfirstlane((int)(min(end, S + L) - S));
+        p.p0 = t_first + __builtin_amdgcn_readfirstlane((int)(pos - S));
+        p.p1 = t_first + p1;
         p.slot = __builtin_amdgcn_readfirstlane((int)(w - S / Q));  // partial index in the segment
         p.c0 = p.p0 & ~15;
         p.nchunks = (p.p1 - p.c0 + kChunk - 1) / kChunk;            // >= 1
-        p.next = S + p.p1;
+        p.next = S + p1;
         return p;
     };
     const Piece none = {0, 0, 0, 0, 0, 0, 0, end};                  // loads nothing
@@ -561,7 +566,7 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
     hipLaunchKernelGGL((decode_split_kernel<NHB, Rows, Fmt>), dim3(nwg), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(a.q), rows, a.block_table, a.seq_lens, opart, lsepart, prefix, a.B,
                        a.Hq, g, P,
-                       a.scale * kLog2e);
+                       a.scale * kLog2e, a.window > 0 ? a.window : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(64 * kCombineWaves), 0, stream, opart, lsepart, prefix,

@@ -104,6 +104,17 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int B
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+int attn_prefill_window_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,
+                            int Sk, int d, float scale, int window, int dtype, void* stream) {
+    const int st = prefill_check(q, k, v, o, B, Hq, Hkv, Sq, Sk, d, scale, 1, dtype);
+    if (st != GQA_OK) return st;
+    if (window <= 0) return GQA_ERR_INVALID_ARG;
+    gqa::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, d, scale, 1, window};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == GQA_F32 ? gqa::launch_prefill_f32(a, s) : gqa::launch_prefill_bf16(a, s);
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
     if (B <= 0 || Hq <= 0 || d <= 0 || max_seq_len <= 0) return 0;
     return gqa::decode_workspace_bytes(B, Hq, d, max_seq_len);
@@ -118,6 +129,21 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
     if (st != GQA_OK) return st;
     gqa::DecodeArgs a{q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
                       block_table ? max_blocks_per_seq : 0, scale, workspace};
+    const hipError_t e = gqa::launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int attn_decode_window_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, const int32_t* seq_lens,
+                           const int32_t* block_table, int B, int Hq, int Hkv, int d, int max_seq_len,
+                           int block_size, int max_blocks_per_seq, float scale, int window, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = decode_check(q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
+                                block_size, max_blocks_per_seq, scale, dtype, workspace, workspace_bytes);
+    if (st != GQA_OK) return st;
+    if (window <= 0) return GQA_ERR_INVALID_ARG;
+    gqa::DecodeArgs a{q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
+                      block_table ? max_blocks_per_seq : 0, scale, workspace};
+    a.window = window;
     const hipError_t e = gqa::launch_decode_bf16(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

@@ -15,6 +15,7 @@ struct PrefillArgs {
     int B, Hq, Hkv, Sq, Sk, d;
     float scale;
     int causal;
+    int window = 0;                 // > 0: sliding window of that many keys (implies causal)
 };
 
 struct DecodeArgs {
@@ -31,6 +32,7 @@ struct DecodeArgs {
     void* workspace;
     const float* k_scale = nullptr;   // fp8 caches: per-row scales, same row numbering as the cache
     const float* v_scale = nullptr;
+    int window = 0;                   // > 0: attend only each sequence's last `window` tokens
 };
 
 // Decode work partition.  The flattened space of (sequence, K/V head, token)

@@ -150,11 +150,11 @@ __device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
 }
 
-template <int D>
+template <int D, bool kWindow>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, int lg, int nqb, int by_cost,
-    float scale_log2, int causal) {
+    float scale_log2, int causal, int window) {
     constexpr int kChunks = D / 8;                          // 16-byte chunks per row
     constexpr int kDSteps = D / 16;                         // MFMA contraction steps over d
     constexpr int kDTiles = D / 32;                         // 32-row output tiles of O^T
@@ -208,19 +208,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int p0 = qb * npos;
     const int off = Sk - Sq;                // causal: key j visible iff j <= pos + off
 
-    // Last visible key of this lane's two query columns.
+    // Sliding window (window > 0, causal): position pos sees keys
+    // (pos + off - window, pos + off].  Keys are counted from kb0, the first
+    // tile holding a key of the workgroup's first row, so the tiles before
+    // it are neither loaded nor computed.
+    const int kb0 = kWindow ? max(0, p0 + off - window + 1) & ~(kBc - 1) : 0;
+
+    // Last visible key of this lane's two query columns (counted from kb0).
     int my_last[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int r = 64 * wave + 32 * nb + n;
-        my_last[nb] = causal ? p0 + (r >> lg) + off : Sk - 1;
+        my_last[nb] = (causal ? p0 + (r >> lg) + off : Sk - 1) - kb0;
     }
 
-    // Keys this workgroup needs; tiles past the wavefront's first diagonal key need the mask.
+    // Keys this workgroup needs; tiles past the wavefront's first diagonal
+    // key, or (window) before its last row's first key, need the mask.
     const int p_last = min(p0 + npos, Sq) - 1;
     const int kend = causal ? min(Sk, p_last + off + 1) : Sk;
-    const int ntiles = (kend + kBc - 1) / kBc;
-    const int wave_first_last = causal ? min(p0 + ((64 * wave) >> lg) + off, Sk - 1) : Sk - 1;
+    const int ntiles = (kend - kb0 + kBc - 1) / kBc;
+    const int wave_first_last = (causal ? min(p0 + ((64 * wave) >> lg) + off, Sk - 1) : Sk - 1) - kb0;
 
     // ---- staging -------------------------------------------------------
     // A direct load moves 16 bytes per lane into consecutive LDS slots
@@ -230,9 +237,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // that the final steps address) are not fetched.  The K/V tiles are
     // zero-filled once, so such rows hold zeros or an older tile's finite
     // values, and the mask removes them.
-    const size_t kvbase = ((size_t)b * Hkv + hk) * (size_t)Sk * D;
-    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(k + kvbase, (uint32_t)kend * D * 2);
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + kvbase, (uint32_t)kend * D * 2);
+    const size_t kvbase = ((size_t)b * Hkv + hk) * (size_t)Sk * D + (size_t)kb0 * D;
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(k + kvbase, (uint32_t)(kend - kb0) * D * 2);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + kvbase, (uint32_t)(kend - kb0) * D * 2);
     // Load x of wavefront w fills the 1 KB slot group t = 4x + w, i.e. rows
     // (64 t + lane) / chunks.  Every row of load x is 16x (d = 128) or 32x
     // (d = 64) rows past that of load 0, a multiple of the swizzle period, so
@@ -458,7 +465,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 issue_read(k_read, v_read, ga / kGroups, ga % kGroups, r, ops[ga]);
 
         const int j0 = j * kBc;
-        if (j0 + kBc - 1 > wave_first_last) {
+        // (window) the wavefront's last row sees no key before this one
+        const int wave_last_first = kWindow ? p0 + ((64 * wave_u + 63) >> lg) + off - window + 1 - kb0 : 0;
+        if (j0 + kBc - 1 > wave_first_last || (kWindow && j0 < wave_last_first)) {
+            int lim[2] = {my_last[0], my_last[1]};
+            // (window) taken as new values here, so that nothing derived from
+            // them is computed ahead of the loop and kept in registers
+            if constexpr (kWindow) asm volatile("" : "+v"(lim[0]), "+v"(lim[1]));
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -466,7 +479,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-                        if (key > my_last[nb]) scur[nb][kb][e] = -INFINITY;
+                        // visible: my_last - window < key <= my_last, one unsigned compare
+                        const bool hidden = kWindow ? (uint32_t)(lim[nb] - key) >= (uint32_t)window
+                                                    : key > lim[nb];
+                        if (hidden) scur[nb][kb][e] = -INFINITY;
                     }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -672,6 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+    const int window = a.window > 0 ? a.window : 0;
     const int g = a.Hq / a.Hkv;
     int lg = 0;
     while ((1 << lg) < g) ++lg;
@@ -691,12 +708,14 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
     uint16_t* o = static_cast<uint16_t*>(a.o);
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, q, k, v, o, a.Hq, a.Hkv, a.Sq, a.Sk, lg, nqb,
+                           by_cost, sl, a.causal, window);
+    };
     if (a.d == 64)
-        hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v, o, a.Hq,
-                           a.Hkv, a.Sq, a.Sk, lg, nqb, by_cost, sl, a.causal);
+        window > 0 ? launch(prefill_bf16_kernel<64, true>) : launch(prefill_bf16_kernel<64, false>);
     else
-        hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v, o, a.Hq,
-                           a.Hkv, a.Sq, a.Sk, lg, nqb, by_cost, sl, a.causal);
+        window > 0 ? launch(prefill_bf16_kernel<128, true>) : launch(prefill_bf16_kernel<128, false>);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ constexpr int kKeysF32 = 32;                           // keys per LDS tile
 template <int D>
 __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, float scale_log2, int causal) {
+    float* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, float scale_log2, int causal, int window) {
     constexpr int DL = D / kLanesPerRow;               // dimensions per lane
     __shared__ float ks[kKeysF32][D + 4];
     __shared__ float vs[kKeysF32][D + 4];
@@ -55,15 +55,18 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
     }
     float m = -INFINITY, l = 0.f;
 
-    // Keys this workgroup can see: causal rows see j <= row + (Sk - Sq).
+    // Keys this workgroup can see: causal rows see j <= row + (Sk - Sq); with
+    // a sliding window (window > 0, causal) also j > row + (Sk - Sq) - window,
+    // so the first tile is the one holding the first row's first key.
     int kend = Sk;
     if (causal) {
         const int last_row = min(row0 + kRowsF32, Sq) - 1;
         kend = min(Sk, last_row + (Sk - Sq) + 1);
     }
     const int my_last = causal ? row + (Sk - Sq) : Sk - 1;
+    const int kbeg = window > 0 ? max(0, row0 + (Sk - Sq) - window + 1) / kKeysF32 * kKeysF32 : 0;
 
-    for (int j0 = 0; j0 < kend; j0 += kKeysF32) {
+    for (int j0 = kbeg; j0 < kend; j0 += kKeysF32) {
         __syncthreads();
         for (int e = tid; e < kKeysF32 * D / 4; e += kThreadsF32) {
             const int r = e / (D / 4), c = 4 * (e % (D / 4));
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
 #pragma unroll
             for (int x = 1; x < kLanesPerRow; x <<= 1) dot += __shfl_xor(dot, x, 64);
             const int j = j0 + r;
-            const bool vis = (j < Sk) && (j <= my_last);
+            const bool vis = (j < Sk) && (j <= my_last) && (window <= 0 || j > my_last - window);
             s[r] = vis ? dot * scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, s[r]);
         }
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
 }  // namespace
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
+    const int window = a.window > 0 ? a.window : 0;
     dim3 grid((a.Sq + kRowsF32 - 1) / kRowsF32, a.Hq, a.B);
     const float sl = a.scale * kLog2e;
     const float* q = static_cast<const float*>(a.q);
@@ -125,10 +129,10 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
     float* o = static_cast<float*>(a.o);
     if (a.d == 64)
         hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv,
-                           a.Sq, a.Sk, sl, a.causal);
+                           a.Sq, a.Sk, sl, a.causal, window);
     else
         hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv,
-                           a.Sq, a.Sk, sl, a.causal);
+                           a.Sq, a.Sk, sl, a.causal, window);
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ EXPORTS = ("gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
            "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks", "gqa_kv_seq_new",
            "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len", "gqa_kv_reserve", "gqa_kv_block_table",
            "attn_kv_append", "attn_kv_copy_blocks", "attn_decode_fp8_fwd", "attn_kv_append_fp8",
-           "attn_kv_copy_blocks_fp8")
+           "attn_kv_copy_blocks_fp8", "attn_prefill_window_fwd", "attn_decode_window_fwd")
 
 _lib = None
 
@@ -86,6 +86,11 @@ def load_library(path: str = LIB_PATH):
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 5 + [vp]
     lib.attn_kv_copy_blocks.restype = c_int
     lib.attn_kv_copy_blocks.argtypes = [vp, vp, vp, vp] + [c_int] * 5 + [vp]
+    lib.attn_prefill_window_fwd.restype = c_int
+    lib.attn_prefill_window_fwd.argtypes = [vp, vp, vp, vp] + [c_int] * 6 + [c_float, c_int, c_int, vp]
+    lib.attn_decode_window_fwd.restype = c_int
+    lib.attn_decode_window_fwd.argtypes = [vp, vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp,
+                                                                                   c_size, vp]
     lib.attn_decode_fp8_fwd.restype = c_int
     lib.attn_decode_fp8_fwd.argtypes = [vp] * 8 + [c_int] * 7 + [c_float, vp, c_size, vp]
     lib.attn_kv_append_fp8.restype = c_int
@@ -146,10 +151,13 @@ def _stream(stream) -> int:
 
 
 def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None, *,
-                     scale: Optional[float] = None, causal: bool = False, stream=None) -> torch.Tensor:
+                     scale: Optional[float] = None, causal: bool = False, stream=None,
+                     window: Optional[int] = None) -> torch.Tensor:
     """O = softmax(Q K^T * scale) V with grouped K/V heads; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d].
 
-    ``scale`` defaults to 1/sqrt(d).  Returns ``o`` (allocated when None).
+    ``scale`` defaults to 1/sqrt(d).  ``window`` (>= 1): causal sliding
+    window, each query sees its last ``window`` keys (attn_prefill_window_fwd).
+    Returns ``o`` (allocated when None).
     """
     lib = load_library()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -166,10 +174,20 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optio
     code = _dtype_code(q, k, v, o)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if window is not None:
+        st = lib.attn_prefill_window_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk,
+                                         d, float(scale), int(window), code, _stream(stream))
+        _raise(st, "attn_prefill_window_fwd")
+        return o
     st = lib.attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk, d,
                               float(scale), 1 if causal else 0, code, _stream(stream))
     _raise(st, "attn_prefill_fwd")
     return o
+
+
+def attn_prefill_window_fwd(q, k, v, o=None, *, window: int, scale=None, stream=None):
+    """Causal sliding-window attention: each query sees its last ``window`` keys."""
+    return attn_prefill_fwd(q, k, v, o, scale=scale, causal=True, stream=stream, window=window)
 
 
 def attn_decode_workspace_bytes(B: int, Hq: int, d: int, max_seq_len: int) -> int:
@@ -184,8 +202,10 @@ def decode_workspace(B: int, Hq: int, d: int, max_seq_len: int, device="cuda") -
 def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
                     o: Optional[torch.Tensor] = None, *, block_table: Optional[torch.Tensor] = None,
                     max_seq_len: Optional[int] = None, scale: Optional[float] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One query token per sequence over a contiguous or paged KV cache.
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    window: Optional[int] = None) -> torch.Tensor:
+    """One query token per sequence over a contiguous or paged KV cache
+    (``window``: only each sequence's last ``window`` tokens, attn_decode_window_fwd).
 
     q [B,Hq,d]; contiguous k/v_cache [B,Hkv,S_max,d]; paged k/v_cache
     [num_blocks,Hkv,16,d] with block_table int32 [B,max_blocks].  seq_lens
@@ -235,12 +255,24 @@ def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     _dev(workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if window is not None:
+        st = lib.attn_decode_window_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                                        seq_lens.data_ptr(), bt_ptr, B, Hq, Hkv, d, int(max_seq_len), block_size,
+                                        max_blocks, float(scale), int(window), code, workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+        _raise(st, "attn_decode_window_fwd")
+        return o
     st = lib.attn_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
                              seq_lens.data_ptr(), bt_ptr, B, Hq, Hkv, d, int(max_seq_len), block_size,
                              max_blocks, float(scale), code, workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _raise(st, "attn_decode_fwd")
     return o
+
+
+def attn_decode_window_fwd(q, k_cache, v_cache, seq_lens, o=None, *, window: int, **kw):
+    """Decode attending only each sequence's last ``window`` cached tokens."""
+    return attn_decode_fwd(q, k_cache, v_cache, seq_lens, o, window=window, **kw)
 
 
 def attn_decode_validate(seq_lens: torch.Tensor, block_table: Optional[torch.Tensor], max_seq_len: int,
