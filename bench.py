@@ -50,9 +50,9 @@ def parse():
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload separately (one JSON line each) instead of the step")
-    ap.add_argument("--sweep-kinds", default="prefill,decode,kv,fp8",
+    ap.add_argument("--sweep-kinds", default="prefill,decode,kv,fp8,window",
                     help="comma list of the sweep's parts: prefill, decode, kv (paged KV-cache writes), "
-                         "fp8 (decode over fp8 caches)")
+                         "fp8 (decode over fp8 caches), window (sliding-window prefill and decode)")
     return ap.parse_args()
 
 
@@ -195,6 +195,64 @@ def sweep(args):
         sweep_kv(args, timed, dev, stream)
     if "fp8" in kinds:
         sweep_fp8(args, dev, stream, flush)
+    if "window" in kinds:
+        sweep_window(args, timed, dev, stream, flush)
+
+
+def sweep_window(args, timed, dev, stream, flush, window=4096):
+    """Sliding-window attention (each query sees its last `window` keys): the
+    GQA S = 8192 prefill workload and the paged Hkv 8 decode workload.  Work
+    counts only the keys inside the windows."""
+    import torch
+    from transformer_exact_attention_amd import gqa_attn
+    from transformer_exact_attention_amd import workloads as W
+    w = W.CFG3
+    log(f"sweep window {window} {w.name}")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+               for x in W.prefill_inputs(w))
+    o = torch.empty_like(q)
+    t = timed(lambda: gqa_attn.attn_prefill_window_fwd(q, k, v, o, window=window, scale=w.scale_value,
+                                                       stream=stream), args.steps)
+    pairs = sum(min(i + 1, window) for i in range(w.Sq))
+    flops = 4.0 * w.d * w.Hq * w.B * pairs
+    tf = flops / float(np.mean(t)) / 1e12
+    print(json.dumps({"workload": f"{w.name}_window{window}", "kind": "prefill_window", "dtype": "bf16",
+                      "flops": flops, "avg_us": round(float(np.mean(t)) * 1e6, 2),
+                      "min_us": round(float(np.min(t)) * 1e6, 2), "TFLOPs": round(tf, 2),
+                      "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    w = W.cfg5(8)
+    log(f"sweep window {window} {w.name}")
+    di = W.decode_inputs(w)
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, kc, vc = g(di.q), g(di.k_cache), g(di.v_cache)
+    lens = torch.from_numpy(di.seq_lens).to(dev)
+    bt = torch.from_numpy(di.block_table).to(dev)
+    o = torch.empty_like(q)
+    ws = gqa_attn.decode_workspace(w.B, w.Hq, w.d, di.max_seq_len, dev)
+    nbytes = int(np.minimum(di.seq_lens, window).sum()) * w.Hkv * w.d * 2 * 2
+    msl = di.max_seq_len
+    del di
+    ev = []
+    for it in range(args.warmup + args.steps):
+        flush.fill_(1)                      # evict the 256 MB Infinity Cache before every call
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gqa_attn.attn_decode_window_fwd(q, kc, vc, lens, o, window=window, block_table=bt, max_seq_len=msl,
+                                        scale=w.scale_value, workspace=ws, stream=stream)
+        b.record(stream)
+        if it >= args.warmup:
+            ev.append((a, b))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    gbs = nbytes / float(np.mean(t)) / 1e9
+    print(json.dumps({"workload": f"{w.name}_window{window}", "kind": "decode_window", "kv_bytes": nbytes,
+                      "avg_us": round(float(np.mean(t)) * 1e6, 2), "min_us": round(float(np.min(t)) * 1e6, 2),
+                      "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                      "tokens_per_s": round(w.B / float(np.mean(t)), 1)}), flush=True)
+    del q, kc, vc, lens, bt, o, ws
+    torch.cuda.empty_cache()
 
 
 def sweep_fp8(args, dev, stream, flush):

@@ -26,7 +26,7 @@ constexpr int kThreadsF32 = 256;
 constexpr int kRowsF32 = kThreadsF32 / kLanesPerRow;   // query rows per workgroup
 constexpr int kKeysF32 = 32;                           // keys per LDS tile
 
-template <int D>
+template <int D, bool kWindow>
 __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, float scale_log2, int causal, int window) {
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
         kend = min(Sk, last_row + (Sk - Sq) + 1);
     }
     const int my_last = causal ? row + (Sk - Sq) : Sk - 1;
-    const int kbeg = window > 0 ? max(0, row0 + (Sk - Sq) - window + 1) / kKeysF32 * kKeysF32 : 0;
+    const int kbeg = kWindow ? max(0, row0 + (Sk - Sq) - window + 1) / kKeysF32 * kKeysF32 : 0;
 
     for (int j0 = kbeg; j0 < kend; j0 += kKeysF32) {
         __syncthreads();
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
 #pragma unroll
             for (int x = 1; x < kLanesPerRow; x <<= 1) dot += __shfl_xor(dot, x, 64);
             const int j = j0 + r;
-            const bool vis = (j < Sk) && (j <= my_last) && (window <= 0 || j > my_last - window);
+            const bool vis = (j < Sk) && (j <= my_last) && (!kWindow || j > my_last - window);
             s[r] = vis ? dot * scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, s[r]);
         }
@@ -127,12 +127,14 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
     const float* k = static_cast<const float*>(a.k);
     const float* v = static_cast<const float*>(a.v);
     float* o = static_cast<float*>(a.o);
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv, a.Sq, a.Sk, sl,
+                           a.causal, window);
+    };
     if (a.d == 64)
-        hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv,
-                           a.Sq, a.Sk, sl, a.causal, window);
+        window > 0 ? launch(prefill_f32_kernel<64, true>) : launch(prefill_f32_kernel<64, false>);
     else
-        hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv,
-                           a.Sq, a.Sk, sl, a.causal, window);
+        window > 0 ? launch(prefill_f32_kernel<128, true>) : launch(prefill_f32_kernel<128, false>);
     return hipGetLastError();
 }
 
