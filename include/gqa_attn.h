@@ -51,7 +51,7 @@ typedef enum {
 
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
 
-#define GQA_ATTN_ABI_VERSION 2
+#define GQA_ATTN_ABI_VERSION 3
 #define GQA_PAGE_BLOCK_SIZE 16   /* tokens per KV page */
 
 /* Version of this ABI (GQA_ATTN_ABI_VERSION of the built library). */
@@ -94,6 +94,54 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o,
 int attn_prefill_window_fwd(const void* q, const void* k, const void* v, void* o,
                             int B, int Hq, int Hkv, int Sq, int Sk, int d,
                             float scale, int window, int dtype, void* stream);
+
+/*
+ * Forward that also writes each query row's natural-log log-sum-exp,
+ *   lse[b, h, i] = log sum_j exp(scale * q_i . k_j)   over visible keys j,
+ * the one number per row the backward needs to recompute the probabilities
+ * without storing them [Attention variants deep-dive, §6.2 technique 2
+ * (recomputation)].  lse: fp32 [B, Hq, Sq], device, written in full (every
+ * row sees at least one key under the rules below).  window == 0: exactly
+ * attn_prefill_fwd (same kernels, same o bit for bit); window >= 1: exactly
+ * attn_prefill_window_fwd (causal implied).  Errors as those calls, plus
+ * GQA_ERR_INVALID_ARG for a NULL lse or window < 0.
+ */
+int attn_prefill_lse_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                         float scale, int causal, int window, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_prefill_bwd needs (fp32 row sums
+ * [B, Hq, Sq], rounded up to 256).  0 on invalid sizes.
+ */
+size_t attn_prefill_bwd_workspace_bytes(int B, int Hq, int Sq);
+
+/*
+ * Backward of attn_prefill_lse_fwd by recomputation: no attention matrix is
+ * kept from the forward; the probabilities are recomputed tile by tile from
+ * q, k and the saved lse, so memory stays linear in the sequence length
+ * [Attention variants deep-dive, §6.2 technique 2; §8 follow-ups 2-3].
+ * With P the forward's probabilities and dO = dout:
+ *   dv = P^T dO,  dP = dO v^T,  dS = P * (dP - rowsum(dO * o)),
+ *   dq = scale dS k,  dk = scale dS^T q,
+ * and a K/V head's dk, dv sum over the g query heads that read it.
+ *
+ *   q, o, dout, dq : [B, Hq, Sq, d]     k, v, dk, dv : [B, Hkv, Sk, d]   (bf16)
+ *   lse            : fp32 [B, Hq, Sq] from attn_prefill_lse_fwd with the same
+ *                    q, k, v, scale, causal and window
+ *   workspace      : device, >= attn_prefill_bwd_workspace_bytes(B, Hq, Sq)
+ *                    bytes, 256-byte aligned; contents on entry are ignored.
+ * dq, dk, dv are overwritten (not accumulated into) and must not overlap any
+ * input.  Supported: GQA_BF16, d in {64, 128}, B * Hq * Sq < 2^27, group
+ * sizes as attn_prefill_fwd.  GQA_ERR_INVALID_ARG as attn_prefill_lse_fwd
+ * and for NULL dout/dq/dk/dv; GQA_ERR_UNSUPPORTED for GQA_F32;
+ * GQA_ERR_WORKSPACE for a short, NULL or misaligned workspace.
+ */
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                     float scale, int causal, int window, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace attn_decode_fwd needs for these sizes (an upper

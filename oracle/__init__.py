@@ -8,3 +8,4 @@ from .core import (  # noqa: F401
     combine_partials, decode_contiguous, decode_paged, default_scale, flash_forward_replay,
     kv_cache_bytes, kv_head_index, paged_logical_rows, split_partials, to_f64, window_visible,
 )
+from .backward import attention_backward, attention_backward_sampled, gradient_magnitudes, row_dot  # noqa: F401,E402

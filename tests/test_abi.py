@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                             "gqa_kv_seq_new", "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len",
                             "gqa_kv_reserve", "gqa_kv_block_table", "attn_kv_append", "attn_kv_copy_blocks",
                             "attn_decode_fp8_fwd", "attn_kv_append_fp8", "attn_kv_copy_blocks_fp8",
-                            "attn_prefill_window_fwd", "attn_decode_window_fwd"])
+                            "attn_prefill_window_fwd", "attn_decode_window_fwd", "attn_prefill_lse_fwd",
+                            "attn_prefill_bwd_workspace_bytes", "attn_prefill_bwd"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -168,3 +169,39 @@ def test_decode_window_rejects_on_host(lib, kw, status):
     assert lib.attn_decode_window_fwd(a["q"], a["k"], a["v"], a["o"], a["lens"], a["table"], a["B"], a["Hq"],
                                       a["Hkv"], a["d"], a["max_seq_len"], a["block_size"], a["max_blocks"],
                                       a["scale"], a["window"], a["dtype"], a["ws"], a["ws_bytes"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(lse=None), 1), (dict(window=-1), 1), (dict(Sq=17, Sk=16, window=4), 1),
+                                       (dict(q=None), 1), (dict(d=96), 2), (dict(dtype=5), 1)])
+def test_prefill_lse_rejects_on_host(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=16, Sk=16, d=64, scale=0.125, causal=0,
+             window=0, dtype=1)
+    a.update(kw)
+    assert lib.attn_prefill_lse_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                                    a["Sk"], a["d"], a["scale"], a["causal"], a["window"], a["dtype"], None) == status
+
+
+def bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, Sq=16,
+             Sk=16, d=64, scale=0.125, causal=1, window=0, dtype=1, ws=0x100000 * 256, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.attn_prefill_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"],
+                                a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["window"],
+                                a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(k=None), 1), (dict(window=-2), 1), (dict(Sq=32, Sk=16), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(scale=0.0), 1), (dict(dtype=0), 2), (dict(d=96), 2), (dict(B=2048, Hq=128, Hkv=128, Sq=1024, Sk=1024), 2),
+    (dict(ws=None), 3), (dict(ws=0x100000 * 256 + 64), 3), (dict(ws_bytes=16 * 4 * 4 - 4), 3),
+])
+def test_prefill_bwd_rejects_on_host(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_prefill_bwd_workspace_formula(lib):
+    assert lib.attn_prefill_bwd_workspace_bytes(1, 4, 16) == 256
+    assert lib.attn_prefill_bwd_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 4
+    assert lib.attn_prefill_bwd_workspace_bytes(1, 1, 65) == 512
+    assert lib.attn_prefill_bwd_workspace_bytes(0, 4, 16) == 0

@@ -103,3 +103,51 @@ def test_dropped_term_fails_a_pin(monkeypatch):
         monkeypatch.setattr(BW, "attention_backward", mutant)
         with pytest.raises(AssertionError):
             test_gradients_match_central_differences(False, None, 5, 6)
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 5)])
+def test_sampled_backward_agrees_with_the_full_one(causal, window):
+    """The restricted products pick out exactly the full gradients' entries."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, Sq, Sk, d = 2, 6, 2, 9, 13, 4
+    q = rng.standard_normal((B, Hq, Sq, d))
+    k = rng.standard_normal((B, Hkv, Sk, d))
+    v = rng.standard_normal((B, Hkv, Sk, d))
+    do = rng.standard_normal((B, Hq, Sq, d))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=causal, window=window)
+    rows, keys = np.array([0, 4, 8]), np.array([1, 6, 12])
+    for b in range(B):
+        for hk in range(Hkv):
+            sq, sk, sv = oracle.attention_backward_sampled(q, k, v, do, b, hk, rows, keys, causal=causal,
+                                                           window=window)
+            assert sorted(sq) == [h for h in range(Hq) if h // 3 == hk]
+            for h, got in sq.items():
+                np.testing.assert_allclose(got, dq[b, h, rows], atol=1e-12)
+            np.testing.assert_allclose(sk, dk[b, hk, keys], atol=1e-12)
+            np.testing.assert_allclose(sv, dv[b, hk, keys], atol=1e-12)
+
+
+def test_gradient_magnitudes_bound_the_gradients_and_match_sampling():
+    """|gradient| <= magnitude entrywise (triangle inequality), equality when
+    every term is non-negative, and the sampled variant picks the same entries."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, Sq, Sk, d = 1, 4, 2, 7, 11, 3
+    q = rng.standard_normal((B, Hq, Sq, d))
+    k = rng.standard_normal((B, Hkv, Sk, d))
+    v = rng.standard_normal((B, Hkv, Sk, d))
+    do = rng.standard_normal((B, Hq, Sq, d))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=True)
+    mq, mk, mv = oracle.gradient_magnitudes(q, k, v, do, causal=True)
+    for g, m in ((dq, mq), (dk, mk), (dv, mv)):
+        assert np.all(np.abs(g) <= m + 1e-12)
+    # dO >= 0: dv = P^T dO has only non-negative terms
+    _, _, dv_pos = oracle.attention_backward(q, k, v, np.abs(do), causal=True)
+    _, _, mv_pos = oracle.gradient_magnitudes(q, k, v, np.abs(do), causal=True)
+    np.testing.assert_allclose(dv_pos, mv_pos, rtol=1e-12)
+    rows, keys = np.array([0, 6]), np.array([2, 10])
+    _, _, _, (sq, sk, sv) = oracle.attention_backward_sampled(q, k, v, do, 0, 1, rows, keys, causal=True,
+                                                              magnitudes=True)
+    for h in (2, 3):
+        np.testing.assert_allclose(sq[h], mq[0, h, rows], rtol=1e-12)
+    np.testing.assert_allclose(sk, mk[0, 1, keys], rtol=1e-12)
+    np.testing.assert_allclose(sv, mv[0, 1, keys], rtol=1e-12)

@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libgqa_attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
 
-DEVICE_SOURCES = ["prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "kv_cache.hip"]
+DEVICE_SOURCES = ["prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "kv_cache.hip", "backward.hip"]
 HOST_SOURCES = ["gqa_attn.cpp", "kv_cache.cpp"]
 
 # Packed-fp32 VALU forms are disabled on purpose (-packed-fp32-ops); the host

@@ -115,6 +115,41 @@ int attn_prefill_window_fwd(const void* q, const void* k, const void* v, void* o
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+int attn_prefill_lse_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                         int Sq, int Sk, int d, float scale, int causal, int window, int dtype, void* stream) {
+    if (!lse || window < 0) return GQA_ERR_INVALID_ARG;
+    const int causal_eff = causal != 0 || window > 0 ? 1 : 0;
+    const int st = prefill_check(q, k, v, o, B, Hq, Hkv, Sq, Sk, d, scale, causal_eff, dtype);
+    if (st != GQA_OK) return st;
+    gqa::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, d, scale, causal_eff, window, lse};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == GQA_F32 ? gqa::launch_prefill_f32(a, s) : gqa::launch_prefill_bf16(a, s);
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+size_t attn_prefill_bwd_workspace_bytes(int B, int Hq, int Sq) {
+    if (B <= 0 || Hq <= 0 || Sq <= 0) return 0;
+    return gqa::align256((size_t)B * Hq * Sq * sizeof(float));
+}
+
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale,
+                     int causal, int window, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!o || !lse || !dout || !dq || !dk || !dv || window < 0) return GQA_ERR_INVALID_ARG;
+    const int causal_eff = causal != 0 || window > 0 ? 1 : 0;
+    // o only marks the output argument of the shared check; q, k, v are read.
+    const int st = prefill_check(q, k, v, dq, B, Hq, Hkv, Sq, Sk, d, scale, causal_eff, dtype);
+    if (st != GQA_OK) return st;
+    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * Sq >= ((int64_t)1 << 27)) return GQA_ERR_UNSUPPORTED;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GQA_ERR_WORKSPACE;
+    if (workspace_bytes < attn_prefill_bwd_workspace_bytes(B, Hq, Sq)) return GQA_ERR_WORKSPACE;
+    gqa::BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
+                        B, Hq, Hkv, Sq, Sk, d, scale, causal_eff, window};
+    const hipError_t e = gqa::launch_prefill_bwd_bf16(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
     if (B <= 0 || Hq <= 0 || d <= 0 || max_seq_len <= 0) return 0;
     return gqa::decode_workspace_bytes(B, Hq, d, max_seq_len);

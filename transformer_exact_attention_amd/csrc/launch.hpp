@@ -16,6 +16,25 @@ struct PrefillArgs {
     float scale;
     int causal;
     int window = 0;                 // > 0: sliding window of that many keys (implies causal)
+    float* lse = nullptr;           // optional: natural-log log-sum-exp per (b, head, row), fp32
+};
+
+// Backward of prefill attention (bf16 tensors, fp32 lse and row sums).
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;               // natural-log log-sum-exp of the forward, [B, Hq, Sq]
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;                    // workspace: rowsum(dO * O), [B, Hq, Sq] fp32
+    int B, Hq, Hkv, Sq, Sk, d;
+    float scale;
+    int causal;
+    int window;                     // > 0: sliding window (implies causal)
 };
 
 struct DecodeArgs {
@@ -100,5 +119,6 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_copy_blocks(const KvCopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_fp8(const KvAppendArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bwd_bf16(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace gqa

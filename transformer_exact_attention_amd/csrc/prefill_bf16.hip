@@ -154,7 +154,7 @@ template <int D, bool kWindow>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, int lg, int nqb, int by_cost,
-    float scale_log2, int causal, int window) {
+    float scale_log2, int causal, int window, float* __restrict__ lse) {
     constexpr int kChunks = D / 8;                          // 16-byte chunks per row
     constexpr int kDSteps = D / 16;                         // MFMA contraction steps over d
     constexpr int kDTiles = D / 32;                         // 32-row output tiles of O^T
@@ -650,6 +650,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     for (int nb = 0; nb < 2; ++nb) {
         const float lt = l[nb] + __shfl_xor(l[nb], 32, 64);
         inv[nb] = lt > 0.f ? 1.f / lt : 0.f;
+        // Optional log-sum-exp of the row (natural log): ln(sum_j e^{s_j})
+        // = ln 2 * (ref + log2(l)), the value a backward pass needs to
+        // recompute the probabilities.
+        if (lse && hh == 0) {
+            const int r = 64 * wave + 32 * nb + n;
+            const int pos = p0 + (r >> lg);
+            if (pos < Sq)
+                lse[((size_t)b * Hq + hk * g + (r & (g - 1))) * Sq + pos] =
+                    (ref[nb] + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
     }
     constexpr int kUnits = D / 4;                           // 8-byte units per row
     lds_char* const obuf = (lds_char*)q_s + wave_u * (64 * D * 2);
@@ -710,7 +720,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     uint16_t* o = static_cast<uint16_t*>(a.o);
     auto launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, q, k, v, o, a.Hq, a.Hkv, a.Sq, a.Sk, lg, nqb,
-                           by_cost, sl, a.causal, window);
+                           by_cost, sl, a.causal, window, a.lse);
     };
     if (a.d == 64)
         window > 0 ? launch(prefill_bf16_kernel<64, true>) : launch(prefill_bf16_kernel<64, false>);

@@ -29,7 +29,8 @@ constexpr int kKeysF32 = 32;                           // keys per LDS tile
 template <int D, bool kWindow>
 __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, float scale_log2, int causal, int window) {
+    float* __restrict__ o, int Hq, int Hkv, int Sq, int Sk, float scale_log2, int causal, int window,
+    float* __restrict__ lse) {
     constexpr int DL = D / kLanesPerRow;               // dimensions per lane
     __shared__ float ks[kKeysF32][D + 4];
     __shared__ float vs[kKeysF32][D + 4];
@@ -114,6 +115,8 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int i = 0; i < DL; ++i) o[qoff + (size_t)row * D + sub * DL + i] = acc[i] * inv;
+        // optional natural-log log-sum-exp of the row: ln 2 * (m + log2 l)
+        if (lse && sub == 0) lse[((size_t)b * Hq + h) * Sq + row] = (m + __builtin_amdgcn_logf(l)) * kLn2;
     }
 }
 
@@ -129,7 +132,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
     float* o = static_cast<float*>(a.o);
     auto launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(kThreadsF32), 0, stream, q, k, v, o, a.Hq, a.Hkv, a.Sq, a.Sk, sl,
-                           a.causal, window);
+                           a.causal, window, a.lse);
     };
     if (a.d == 64)
         window > 0 ? launch(prefill_f32_kernel<64, true>) : launch(prefill_f32_kernel<64, false>);

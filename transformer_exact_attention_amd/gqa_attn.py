@@ -28,7 +28,8 @@ EXPORTS = ("gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
            "gqa_kv_pool_create", "gqa_kv_pool_destroy", "gqa_kv_pool_free_blocks", "gqa_kv_seq_new",
            "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len", "gqa_kv_reserve", "gqa_kv_block_table",
            "attn_kv_append", "attn_kv_copy_blocks", "attn_decode_fp8_fwd", "attn_kv_append_fp8",
-           "attn_kv_copy_blocks_fp8", "attn_prefill_window_fwd", "attn_decode_window_fwd")
+           "attn_kv_copy_blocks_fp8", "attn_prefill_window_fwd", "attn_decode_window_fwd",
+           "attn_prefill_lse_fwd", "attn_prefill_bwd_workspace_bytes", "attn_prefill_bwd")
 
 _lib = None
 
@@ -97,6 +98,12 @@ def load_library(path: str = LIB_PATH):
     lib.attn_kv_append_fp8.argtypes = [vp] * 7 + [c_int] * 4 + [vp]
     lib.attn_kv_copy_blocks_fp8.restype = c_int
     lib.attn_kv_copy_blocks_fp8.argtypes = [vp] * 6 + [c_int] * 4 + [vp]
+    lib.attn_prefill_lse_fwd.restype = c_int
+    lib.attn_prefill_lse_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, c_int, c_int, c_int, vp]
+    lib.attn_prefill_bwd_workspace_bytes.restype = c_size
+    lib.attn_prefill_bwd_workspace_bytes.argtypes = [c_int] * 3
+    lib.attn_prefill_bwd.restype = c_int
+    lib.attn_prefill_bwd.argtypes = [vp] * 9 + [c_int] * 6 + [c_float, c_int, c_int, c_int, vp, c_size, vp]
     _lib = lib
     return lib
 
@@ -188,6 +195,82 @@ def attn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optio
 def attn_prefill_window_fwd(q, k, v, o=None, *, window: int, scale=None, stream=None):
     """Causal sliding-window attention: each query sees its last ``window`` keys."""
     return attn_prefill_fwd(q, k, v, o, scale=scale, causal=True, stream=stream, window=window)
+
+
+def _prefill_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, d]")
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    return B, Hq, Hkv, Sq, Sk, d
+
+
+def attn_prefill_lse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, *, scale: Optional[float] = None, causal: bool = False,
+                         window: int = 0, stream=None):
+    """Forward that also returns the per-row natural-log log-sum-exp [B, Hq, Sq] (fp32).
+
+    Same output as attn_prefill_fwd (window 0) or attn_prefill_window_fwd
+    (window >= 1, causal implied).  Returns ``(o, lse)``.
+    """
+    lib = load_library()
+    B, Hq, Hkv, Sq, Sk, d = _prefill_shapes(q, k, v)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("o must have q's shape and lse be float32 [B, Hq, Sq]")
+    _dev(q, k, v, o, lse)
+    code = _dtype_code(q, k, v, o)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_prefill_lse_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                                  Sq, Sk, d, float(scale), 1 if causal else 0, int(window), code, _stream(stream))
+    _raise(st, "attn_prefill_lse_fwd")
+    return o, lse
+
+
+def attn_prefill_bwd_workspace_bytes(B: int, Hq: int, Sq: int) -> int:
+    return int(load_library().attn_prefill_bwd_workspace_bytes(B, Hq, Sq))
+
+
+def attn_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                     dout: torch.Tensor, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                     dv: Optional[torch.Tensor] = None, *, scale: Optional[float] = None, causal: bool = False,
+                     window: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) of attn_prefill_lse_fwd for output gradient ``dout`` (bf16).
+
+    ``o`` and ``lse`` are the forward's outputs for the same q, k, v, scale,
+    causal and window.  Returns ``(dq, dk, dv)`` (allocated when None).
+    """
+    lib = load_library()
+    B, Hq, Hkv, Sq, Sk, d = _prefill_shapes(q, k, v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(dq.shape) != tuple(q.shape):
+        raise ValueError("o, dout and dq must have q's shape")
+    if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("dk and dv must have k's shape")
+    if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Sq]")
+    _dev(q, k, v, o, lse, dout, dq, dk, dv)
+    code = _dtype_code(q, k, v, o, dout, dq, dk, dv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_prefill_bwd_workspace_bytes(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace)
+    st = lib.attn_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Sk, d,
+                              float(scale), 1 if causal else 0, int(window), code, workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise(st, "attn_prefill_bwd")
+    return dq, dk, dv
 
 
 def attn_decode_workspace_bytes(B: int, Hq: int, d: int, max_seq_len: int) -> int:
