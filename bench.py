@@ -50,7 +50,7 @@ def parse():
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload separately (one JSON line each) instead of the step")
-    ap.add_argument("--sweep-kinds", default="prefill,decode,kv,fp8,window",
+    ap.add_argument("--sweep-kinds", default="prefill,decode,kv,fp8,window,bwd",
                     help="comma list of the sweep's parts: prefill, decode, kv (paged KV-cache writes), "
                          "fp8 (decode over fp8 caches), window (sliding-window prefill and decode)")
     return ap.parse_args()
@@ -197,6 +197,8 @@ def sweep(args):
         sweep_fp8(args, dev, stream, flush)
     if "window" in kinds:
         sweep_window(args, timed, dev, stream, flush)
+    if "bwd" in kinds:
+        sweep_bwd(args, timed, dev, stream)
 
 
 def sweep_window(args, timed, dev, stream, flush, window=4096):
@@ -253,6 +255,38 @@ def sweep_window(args, timed, dev, stream, flush, window=4096):
                       "tokens_per_s": round(w.B / float(np.mean(t)), 1)}), flush=True)
     del q, kc, vc, lens, bt, o, ws
     torch.cuda.empty_cache()
+
+
+def sweep_bwd(args, timed, dev, stream):
+    """Backward by recomputation on the two bf16 prefill workloads.  Work is
+    the usual count of five products per visible (query, key) pair (S
+    recomputed, dP, dV, dK, dQ: 2.5 x the forward); the kernels actually
+    recompute S and dP once more for dQ (seven products), so the executed
+    rate is 1.4 x the reported one."""
+    import torch
+    from transformer_exact_attention_amd import gqa_attn
+    from transformer_exact_attention_amd import workloads as W
+    for w in (W.CFG2, W.CFG3):
+        log(f"sweep backward {w.name}")
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+                   for x in W.prefill_inputs(w))
+        do = torch.from_numpy(W.normal([w.seed, 9], (w.B, w.Hq, w.Sq, w.d), "bf16").view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        o, lse = gqa_attn.attn_prefill_lse_fwd(q, k, v, scale=w.scale_value, causal=w.causal, stream=stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(gqa_attn.attn_prefill_bwd_workspace_bytes(w.B, w.Hq, w.Sq), dtype=torch.uint8, device=dev)
+        tf_fwd = timed(lambda: gqa_attn.attn_prefill_lse_fwd(q, k, v, o, lse, scale=w.scale_value, causal=w.causal,
+                                                             stream=stream), args.steps)
+        t = timed(lambda: gqa_attn.attn_prefill_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=w.scale_value,
+                                                    causal=w.causal, workspace=ws, stream=stream), args.steps)
+        flops = 2.5 * w.flops()
+        tf = flops / float(np.mean(t)) / 1e12
+        print(json.dumps({"workload": w.name, "kind": "backward", "dtype": "bf16", "flops": flops,
+                          "avg_us": round(float(np.mean(t)) * 1e6, 2), "min_us": round(float(np.min(t)) * 1e6, 2),
+                          "TFLOPs": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "lse_forward_avg_us": round(float(np.mean(tf_fwd)) * 1e6, 2)}), flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
 
 
 def sweep_fp8(args, dev, stream, flush):

@@ -132,7 +132,8 @@ size_t attn_prefill_bwd_workspace_bytes(int B, int Hq, int Sq);
  *   workspace      : device, >= attn_prefill_bwd_workspace_bytes(B, Hq, Sq)
  *                    bytes, 256-byte aligned; contents on entry are ignored.
  * dq, dk, dv are overwritten (not accumulated into) and must not overlap any
- * input.  Supported: GQA_BF16, d in {64, 128}, B * Hq * Sq < 2^27, group
+ * input.  Supported: GQA_BF16, d in {64, 128}, B * Hq * Sq < 2^27,
+ * ceil(Sk / 128) * Hkv * B < 2^31, group
  * sizes as attn_prefill_fwd.  GQA_ERR_INVALID_ARG as attn_prefill_lse_fwd
  * and for NULL dout/dq/dk/dv; GQA_ERR_UNSUPPORTED for GQA_F32;
  * GQA_ERR_WORKSPACE for a short, NULL or misaligned workspace.

@@ -44,18 +44,34 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 constexpr int kBwdThreads = 256;
 constexpr int kTileRows = 64;            // rows of a staged tile (4 wavefronts x 16)
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
+// LDS tile of 64 rows x D bf16.  Operands are read two ways: 16-byte row
+// pieces of 16 consecutive rows at one column (ds_read_b128), and 8-byte
+// pieces of 4 consecutive rows x 32 columns (transposing reads, two 16-lane
+// groups at a time).  D = 128: rows of 256 bytes with their 16-byte units
+// XOR-swizzled by f(row) = 4 (row % 4) + (row / 4) % 4, a bijection on 16
+// rows (row reads hit 16 distinct 4-bank groups) that moves the 4 rows of a
+// transposing read to disjoint unit groups (all 64 banks once).  D = 64: rows
+// padded to 144 bytes.
 template <int D>
 struct Tile {
-    static constexpr int kRowBytes = D * 2 + 16;
+    static constexpr int kRowBytes = D == 128 ? 256 : D * 2 + 16;
     static constexpr int kBytes = kTileRows * kRowBytes;
+    // byte offset of element `col` (a multiple of 4) of `row`
+    static __device__ __forceinline__ int off(int row, int col) {
+        if constexpr (D == 128) {
+            const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+            return row * kRowBytes + ((((col >> 3) ^ f)) << 4) + ((col & 7) << 1);
+        } else {
+            return row * kRowBytes + 2 * col;
+        }
+    }
 };
 
-// 64 x D bf16 rows [row0, row0 + 64) of a [rows_total, D] matrix -> LDS tile
-// (rows past rows_total are zero).  256 threads, 16-byte chunks.
+// 64 x D bf16 rows [row0, row0 + 64) of a [rows_total, D] matrix -> LDS tile.
+// Rows past rows_total repeat the last row (finite values whose products the
+// callers multiply by a zero probability); the loads stay unconditional, so
+// no branch keeps the compiler from overlapping them with the tile's work.
+// 256 threads, 16-byte chunks.
 template <int D>
 __device__ __forceinline__ void load_rows(u32x4 (&reg)[kTileRows * D / 8 / kBwdThreads], const uint16_t* base,
                                           int row0, int rows_total) {
@@ -64,9 +80,8 @@ __device__ __forceinline__ void load_rows(u32x4 (&reg)[kTileRows * D / 8 / kBwdT
     for (int x = 0; x < kTileRows * kChunks / kBwdThreads; ++x) {
         const int i = x * kBwdThreads + (int)threadIdx.x;
         const int r = i / kChunks, c = i % kChunks;
-        const int row = row0 + r;
-        reg[x] = row < rows_total ? *reinterpret_cast<const u32x4*>(base + (size_t)row * D + 8 * c)
-                                  : u32x4{0u, 0u, 0u, 0u};
+        const int row = min(row0 + r, rows_total - 1);
+        reg[x] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + 8 * c);
     }
 }
 template <int D>
@@ -76,27 +91,8 @@ __device__ __forceinline__ void store_rows(lds_char* tile, const u32x4 (&reg)[kT
     for (int x = 0; x < kTileRows * kChunks / kBwdThreads; ++x) {
         const int i = x * kBwdThreads + (int)threadIdx.x;
         const int r = i / kChunks, c = i % kChunks;
-        *(lds_u32x4*)(tile + r * Tile<D>::kRowBytes + 16 * c) = reg[x];
+        *(lds_u32x4*)(tile + Tile<D>::off(r, 8 * c)) = reg[x];
     }
-}
-// A/B fragment from a row: 4 bf16 at (row, col..col+3).
-template <int D>
-__device__ __forceinline__ bf16x4 row_frag(const lds_char* tile, int row, int col) {
-    return __builtin_bit_cast(bf16x4, *(const lds_u32x2*)(tile + row * Tile<D>::kRowBytes + 2 * col));
-}
-// Column fragment: rows r0 + 4 q4 .. +3 of column col0 + (lane % 16).
-template <int D>
-__device__ __forceinline__ bf16x4 col_frag(const lds_char* tile, int r0, int col0, int lane) {
-    const int g = lane >> 4, r = lane & 15;
-    const int row = r0 + 4 * g + (r >> 2);
-    const int col = col0 + 4 * (r & 3);
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(tile + row * Tile<D>::kRowBytes + 2 * col));
-    return __builtin_bit_cast(bf16x4, v);
-}
-__device__ __forceinline__ bf16x4 pack4(const f32x4& x) {
-    const u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-    return __builtin_bit_cast(bf16x4, w);
 }
 
 // D[row] = sum_d dO[row][d] * O[row][d]; 16 lanes per row (D = 128: 8
@@ -122,7 +118,46 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rowdot_kernel(const uint16_t*
     if (row < rows && sub == 0) dsum[row] = acc;
 }
 
-// dK, dV for 64 keys of K/V head hk of batch b.
+// 32-row operand fragments for v_mfma_f32_32x32x16_bf16 (A: lane l holds
+// row l % 32, k = 8 (l / 32) .. +7; B: k = 8 (l / 32) .. +7 of column l % 32;
+// D: register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4 of column
+// l % 32).  A D-layout result used as the contraction operand of the next
+// product is taken in the order its registers hold it: in 16-row step s,
+// position e of lane half h stands for row
+//   m(s, h, e) = 16 s + 8 (e / 4) + 4 h + e % 4,
+// and the other operand supplies the same rows with two transposing reads
+// (rows 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3).
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// A/B fragment of a row: 8 bf16 at (row, col .. col + 7).
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag8(const lds_char* tile, int row, int col) {
+    return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(tile + Tile<D>::off(row, col)));
+}
+// Column fragment in the m(s, h, e) order: column col0 + (lane % 32) of rows
+// r0 + 16 s + {4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3}.
+template <int D>
+__device__ __forceinline__ bf16x8 col_frag8(const lds_char* tile, int r0, int col0, int lane) {
+    const int grp = lane >> 4, r = lane & 15;
+    const int h = grp >> 1;
+    const int row = r0 + 4 * h + (r >> 2);
+    const int col = col0 + 16 * (grp & 1) + 4 * (r & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + Tile<D>::off(row, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + Tile<D>::off(row + 8, col)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int s) {
+    const u32x4 w = {pack_bf16x2(x[8 * s + 0], x[8 * s + 1]), pack_bf16x2(x[8 * s + 2], x[8 * s + 3]),
+                     pack_bf16x2(x[8 * s + 4], x[8 * s + 5]), pack_bf16x2(x[8 * s + 6], x[8 * s + 7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+constexpr int kWaveRows = 32;                      // keys (dK/dV) or query rows (dQ) per wavefront
+constexpr int kBlockRows = 4 * kWaveRows;          // per workgroup
+
+// dK, dV for 128 keys of K/V head hk of batch b (32 per wavefront).  Query
+// tiles of 64 rows of every head of the group stream through LDS.
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -130,66 +165,78 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int Sq, int Sk, float scale,
     int causal, int window) {
     constexpr int kT = D / 16;                             // 16-wide d steps
+    constexpr int kNT = D / 32;                            // 32-wide d tiles of dK, dV
     constexpr int kRegs = kTileRows * D / 8 / kBwdThreads;
     __shared__ __attribute__((aligned(16))) char q_raw[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char d_raw[2][Tile<D>::kBytes];
-    __shared__ float lse_s[2][kTileRows], dsum_s[2][kTileRows];
+    __shared__ float2 row_s[2][kTileRows];                 // (lse * log2 e, D) per row
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 15, q4 = lane >> 4;
-    const int kb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int n = lane & 31, h = lane >> 5;
+    // 1-D grid, key block slowest: under a causal mask the first key blocks
+    // see the most query rows, so the heaviest workgroups start first
+    const int planes = (int)gridDim.x / ((Sk + kBlockRows - 1) / kBlockRows);     // Hkv * B
+    const int kb = (int)blockIdx.x / planes, hk = (int)blockIdx.x % Hkv, b = ((int)blockIdx.x % planes) / Hkv;
     const int g = Hq / Hkv;
     const int off = Sk - Sq;
-    const int key0 = kb * kTileRows + 16 * wave;           // this wavefront's keys key0 .. key0 + 15
+    const int kw0 = kb * kBlockRows + kWaveRows * wave;    // this wavefront's keys kw0 .. kw0 + 31
+    const int key = kw0 + n;                               // this lane's key column
     const float sl2 = scale * kLog2e;
 
-    // K and V rows of the wavefront's keys as B operands (k = d, column = key c).
-    bf16x4 kf[kT], vf[kT];
+    // K and V rows of the wavefront's keys as B operands (k = d, column = key).
+    bf16x8 kf[kT], vf[kT];
     {
         const size_t kvrow = ((size_t)b * Hkv + hk) * Sk;
-        const int key = key0 + c;
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
-            u32x2 kw = {0u, 0u}, vw = {0u, 0u};
+            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
             if (key < Sk) {
-                kw = *reinterpret_cast<const u32x2*>(k + (kvrow + key) * D + 16 * t + 4 * q4);
-                vw = *reinterpret_cast<const u32x2*>(v + (kvrow + key) * D + 16 * t + 4 * q4);
+                kw = *reinterpret_cast<const u32x4*>(k + (kvrow + key) * D + 16 * t + 8 * h);
+                vw = *reinterpret_cast<const u32x4*>(v + (kvrow + key) * D + 16 * t + 8 * h);
             }
-            kf[t] = __builtin_bit_cast(bf16x4, kw);
-            vf[t] = __builtin_bit_cast(bf16x4, vw);
+            kf[t] = __builtin_bit_cast(bf16x8, kw);
+            vf[t] = __builtin_bit_cast(bf16x8, vw);
         }
-    }
-    f32x4 dka[kT], dva[kT];
+        // Redefine the fragments past their loads: the loop below then sees
+        // registers with no load pending and never waits on the tile
+        // prefetches it has in flight (the wait counter is in order).
 #pragma unroll
-    for (int t = 0; t < kT; ++t) dka[t] = dva[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < kT; ++t) asm volatile("" : "+v"(kf[t]), "+v"(vf[t]));
+    }
+    f32x16 dka[kNT], dva[kNT];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dka[t][r] = dva[t][r] = 0.f;
 
     // Query tiles: for each head of the group, the tiles holding a row that
     // sees one of the workgroup's keys (causal: rows i >= key - off; window W:
     // also i < key - off + W).
-    const int first_tile = causal ? max(0, kb * kTileRows - off) / kTileRows : 0;
+    const int first_tile = causal ? max(0, kb * kBlockRows - off) / kTileRows : 0;
     int end_tile = (Sq + kTileRows - 1) / kTileRows;
-    if (window > 0) end_tile = min(end_tile, max(0, kb * kTileRows + kTileRows - 1 - off + window - 1) / kTileRows + 1);
+    if (window > 0)
+        end_tile = min(end_tile, max(0, kb * kBlockRows + kBlockRows - 1 - off + window - 1) / kTileRows + 1);
     const int n_per_head = max(0, end_tile - first_tile);
     const int total = g * n_per_head;
     u32x4 qr[kRegs], dr[kRegs];
     auto fetch = [&](int it) {
-        const int h = hk * g + it / n_per_head;
+        const int hq = hk * g + it / n_per_head;
         const int row0 = (first_tile + it % n_per_head) * kTileRows;
-        const size_t base = ((size_t)b * Hq + h) * Sq;
+        const size_t base = ((size_t)b * Hq + hq) * Sq;
         load_rows<D>(qr, q + base * D, row0, Sq);
         load_rows<D>(dr, dout + base * D, row0, Sq);
     };
     auto stash = [&](int it, int buf) {
-        const int h = hk * g + it / n_per_head;
+        const int hq = hk * g + it / n_per_head;
         const int row0 = (first_tile + it % n_per_head) * kTileRows;
-        const size_t base = ((size_t)b * Hq + h) * Sq;
+        const size_t base = ((size_t)b * Hq + hq) * Sq;
         store_rows<D>((lds_char*)q_raw[buf], qr);
         store_rows<D>((lds_char*)d_raw[buf], dr);
         if (threadIdx.x < kTileRows) {
             const int row = row0 + threadIdx.x;
             // rows past Sq: lse = +inf makes their probabilities 0
-            lse_s[buf][threadIdx.x] = row < Sq ? lse[base + row] * kLog2e : INFINITY;
-            dsum_s[buf][threadIdx.x] = row < Sq ? dsum[base + row] : 0.f;
+            row_s[buf][threadIdx.x] = row < Sq ? float2{lse[base + row] * kLog2e, dsum[base + row]}
+                                               : float2{INFINITY, 0.f};
         }
     };
     if (total > 0) {
@@ -204,30 +251,58 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         const lds_char* qt = (const lds_char*)q_raw[buf];
         const lds_char* dt = (const lds_char*)d_raw[buf];
 #pragma unroll
-        for (int sub = 0; sub < kTileRows / 16; ++sub) {
-            const int r0 = 16 * sub;                        // query rows row0 + r0 .. +15
-            // S (16 q x 16 keys) = Q K^T; dP = dO V^T
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        for (int sub = 0; sub < kTileRows / kWaveRows; ++sub) {
+            const int r0 = kWaveRows * sub;                 // tile rows r0 .. r0 + 31
+            const int pos0 = row0 + r0;
+            // rows that see none of the wavefront's keys contribute nothing
+            if (causal && pos0 + kWaveRows - 1 + off < kw0) continue;
+            if (window > 0 && pos0 + off - window >= kw0 + kWaveRows - 1) continue;
+            // S (32 rows x 32 keys) = Q K^T; dP = dO V^T
+            f32x16 sc, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
+            bf16x8 qa[kT], da[kT];                          // all operand reads first, one wait
 #pragma unroll
             for (int t = 0; t < kT; ++t) {
-                s = mfma16(row_frag<D>(qt, r0 + c, 16 * t + 4 * q4), kf[t], s);
-                dp = mfma16(row_frag<D>(dt, r0 + c, 16 * t + 4 * q4), vf[t], dp);
+                qa[t] = row_frag8<D>(qt, r0 + n, 16 * t + 8 * h);
+                da[t] = row_frag8<D>(dt, r0 + n, 16 * t + 8 * h);
             }
-            // lane holds rows q = r0 + 4 q4 + r of column key0 + c
-            f32x4 p, ds;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int qi = r0 + 4 * q4 + r;
+            for (int t = 0; t < kT; ++t) {
+                sc = mfma32(qa[t], kf[t], sc);
+                dp = mfma32(da[t], vf[t], dp);
+            }
+            // every (row, key) of the block visible?
+            const bool full = (!causal || pos0 + off >= kw0 + kWaveRows - 1) &&
+                              (window <= 0 || pos0 + kWaveRows - 1 + off - window < kw0);
+            f32x16 p, ds;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const float2 ld = row_s[buf][qi];
                 const int pos = row0 + qi;
-                const bool vis = (!causal || key0 + c <= pos + off) && (window <= 0 || key0 + c > pos + off - window);
-                p[r] = vis ? exp2_fast(fmaf(s[r], sl2, -lse_s[buf][qi])) : 0.f;
-                ds[r] = p[r] * (dp[r] - dsum_s[buf][qi]);
+                // branch-free (a branch would split the scheduling region)
+                const bool vis = full | ((!causal | (key <= pos + off)) & ((window <= 0) | (key > pos + off - window)));
+                const float e = exp2_fast(fmaf(sc[r], sl2, -ld.x));
+                p[r] = vis ? e : 0.f;
+                ds[r] = p[r] * (dp[r] - ld.y);
             }
-            const bf16x4 pa = pack4(p), dsa = pack4(ds);   // P^T, dS^T as A operands (rows = keys)
+            bf16x8 dc[2][kNT], qc[2][kNT];
 #pragma unroll
-            for (int t = 0; t < kT; ++t) {
-                dva[t] = mfma16(pa, col_frag<D>(dt, r0, 16 * t, lane), dva[t]);
-                dka[t] = mfma16(dsa, col_frag<D>(qt, r0, 16 * t, lane), dka[t]);
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) {
+                    dc[s2][t] = col_frag8<D>(dt, r0 + 16 * s2, 32 * t, lane);
+                    qc[s2][t] = col_frag8<D>(qt, r0 + 16 * s2, 32 * t, lane);
+                }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 pa = pack8(p, s2), dsa = pack8(ds, s2);   // P^T, dS^T as A (rows = keys)
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) {
+                    dva[t] = mfma32(pa, dc[s2][t], dva[t]);
+                    dka[t] = mfma32(dsa, qc[s2][t], dka[t]);
+                }
             }
         }
         if (it + 1 < total) {
@@ -236,15 +311,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
             __syncthreads();
         }
     }
-    // rows key0 + 4 q4 + r, columns 16 t + c
+    // register r: key kw0 + 8 (r / 4) + 4 h + r % 4, column 32 t + n
     const size_t kvrow = ((size_t)b * Hkv + hk) * Sk;
 #pragma unroll
-    for (int t = 0; t < kT; ++t)
+    for (int t = 0; t < kNT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 4 * q4 + r;
-            if (key < Sk) {
-                const size_t at = (kvrow + key) * D + 16 * t + c;
+        for (int r = 0; r < 16; ++r) {
+            const int kr = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kr < Sk) {
+                const size_t at = (kvrow + kr) * D + 32 * t + n;
                 const uint32_t pk = pack_bf16x2(dka[t][r] * scale, dva[t][r]);
                 dk[at] = (uint16_t)(pk & 0xffffu);
                 dv[at] = (uint16_t)(pk >> 16);
@@ -252,49 +327,65 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         }
 }
 
-// dQ for 64 query rows of head h of batch b.
+// dQ for 128 query rows of head hq of batch b (32 per wavefront).  Key tiles
+// of 64 keys stream through LDS.
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int Hq, int Hkv, int Sq, int Sk, float scale, int causal, int window) {
     constexpr int kT = D / 16;
+    constexpr int kNT = D / 32;
     constexpr int kRegs = kTileRows * D / 8 / kBwdThreads;
     __shared__ __attribute__((aligned(16))) char k_raw[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char v_raw[2][Tile<D>::kBytes];
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 15, q4 = lane >> 4;
-    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int g = Hq / Hkv, hk = h / g;
+    const int n = lane & 31, h = lane >> 5;
+    // 1-D grid, query block slowest; causal: the last query blocks see the
+    // most keys, so they start first.  The heads of a group are adjacent
+    // (their shared K/V tiles meet in cache).
+    const int nqb = (Sq + kBlockRows - 1) / kBlockRows;
+    const int planes = (int)gridDim.x / nqb;                                      // Hq * B
+    const int rank = (int)blockIdx.x / planes;
+    const int qb = causal ? nqb - 1 - rank : rank;
+    const int hq = (int)blockIdx.x % Hq, b = ((int)blockIdx.x % planes) / Hq;
+    const int g = Hq / Hkv, hk = hq / g;
     const int off = Sk - Sq;
-    const int qrow = qb * kTileRows + 16 * wave + c;       // this lane's query column
+    const int qw0 = qb * kBlockRows + kWaveRows * wave;    // this wavefront's rows qw0 .. qw0 + 31
+    const int qrow = qw0 + n;                              // this lane's query column
     const float sl2 = scale * kLog2e;
-    const size_t qbase = ((size_t)b * Hq + h) * Sq;
+    const size_t qbase = ((size_t)b * Hq + hq) * Sq;
 
-    // Q and dO of the lane's query as B operands (k = d, column = query c).
-    bf16x4 qf[kT], of[kT];
+    // Q and dO of the lane's query as B operands (k = d, column = query).
+    bf16x8 qf[kT], of[kT];
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
-        u32x2 qw = {0u, 0u}, ow = {0u, 0u};
+        u32x4 qw = {0u, 0u, 0u, 0u}, ow = {0u, 0u, 0u, 0u};
         if (qrow < Sq) {
-            qw = *reinterpret_cast<const u32x2*>(q + (qbase + qrow) * D + 16 * t + 4 * q4);
-            ow = *reinterpret_cast<const u32x2*>(dout + (qbase + qrow) * D + 16 * t + 4 * q4);
+            qw = *reinterpret_cast<const u32x4*>(q + (qbase + qrow) * D + 16 * t + 8 * h);
+            ow = *reinterpret_cast<const u32x4*>(dout + (qbase + qrow) * D + 16 * t + 8 * h);
         }
-        qf[t] = __builtin_bit_cast(bf16x4, qw);
-        of[t] = __builtin_bit_cast(bf16x4, ow);
+        qf[t] = __builtin_bit_cast(bf16x8, qw);
+        of[t] = __builtin_bit_cast(bf16x8, ow);
     }
-    const float lse2 = qrow < Sq ? lse[qbase + qrow] * kLog2e : INFINITY;
-    const float dsq = qrow < Sq ? dsum[qbase + qrow] : 0.f;
-    f32x4 dqa[kT];                                         // dQ^T: rows d = 16 t + 4 q4 + r, column = query c
+    float lse2 = qrow < Sq ? lse[qbase + qrow] * kLog2e : INFINITY;
+    float dsq = qrow < Sq ? dsum[qbase + qrow] : 0.f;
+    // as in the dK/dV kernel: no load left pending into the tile loop
 #pragma unroll
-    for (int t = 0; t < kT; ++t) dqa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kT; ++t) asm volatile("" : "+v"(qf[t]), "+v"(of[t]));
+    asm volatile("" : "+v"(lse2), "+v"(dsq));
+    f32x16 dqa[kNT];                                       // dQ^T: register r = d 32 t + 8 (r/4) + 4 h + r % 4
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqa[t][r] = 0.f;
 
     // Key tiles seen by the block's rows (causal: keys <= row + off; window W:
     // also keys > row + off - W).
-    const int q_last = min(qb * kTileRows + kTileRows, Sq) - 1;
+    const int q_last = min(qb * kBlockRows + kBlockRows, Sq) - 1;
     const int kend = causal ? min(Sk, q_last + off + 1) : Sk;
-    const int kfirst = window > 0 ? max(0, qb * kTileRows + off - window + 1) / kTileRows : 0;
+    const int kfirst = window > 0 ? max(0, qb * kBlockRows + off - window + 1) / kTileRows : 0;
     const int ntiles = max(0, (kend + kTileRows - 1) / kTileRows - kfirst);
     const size_t kvbase = ((size_t)b * Hkv + hk) * Sk;
     u32x4 kr[kRegs], vr[kRegs];
@@ -318,27 +409,50 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
         const lds_char* kt = (const lds_char*)k_raw[buf];
         const lds_char* vt = (const lds_char*)v_raw[buf];
 #pragma unroll
-        for (int sub = 0; sub < kTileRows / 16; ++sub) {
-            const int r0 = 16 * sub;                        // keys tile*64 + r0 .. +15
-            // S^T (16 keys x 16 q) = K Q^T; dP^T = V dO^T
-            f32x4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+        for (int sub = 0; sub < kTileRows / kWaveRows; ++sub) {
+            const int r0 = kWaveRows * sub;                 // keys tile * 64 + r0 .. + 31
+            const int key0 = tile * kTileRows + r0;
+            // keys no row of the wavefront sees contribute nothing
+            if (causal && key0 > qw0 + kWaveRows - 1 + off) continue;
+            if (window > 0 && key0 + kWaveRows - 1 <= qw0 + off - window) continue;
+            // S^T (32 keys x 32 rows) = K Q^T; dP^T = V dO^T
+            f32x16 st, dpt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
+            bf16x8 ka[kT], va[kT];                          // all operand reads first, one wait
 #pragma unroll
             for (int t = 0; t < kT; ++t) {
-                st = mfma16(row_frag<D>(kt, r0 + c, 16 * t + 4 * q4), qf[t], st);
-                dpt = mfma16(row_frag<D>(vt, r0 + c, 16 * t + 4 * q4), of[t], dpt);
+                ka[t] = row_frag8<D>(kt, r0 + n, 16 * t + 8 * h);
+                va[t] = row_frag8<D>(vt, r0 + n, 16 * t + 8 * h);
             }
-            // lane holds keys tile*64 + r0 + 4 q4 + r of column qrow
-            f32x4 ds;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = tile * kTileRows + r0 + 4 * q4 + r;
-                const bool vis = key < Sk && (!causal || key <= qrow + off) && (window <= 0 || key > qrow + off - window);
-                const float p = vis ? exp2_fast(fmaf(st[r], sl2, -lse2)) : 0.f;
+            for (int t = 0; t < kT; ++t) {
+                st = mfma32(ka[t], qf[t], st);
+                dpt = mfma32(va[t], of[t], dpt);
+            }
+            const bool full = key0 + kWaveRows - 1 < Sk && (!causal || key0 + kWaveRows - 1 <= qw0 + off) &&
+                              (window <= 0 || key0 > qw0 + kWaveRows - 1 + off - window);
+            f32x16 ds;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool vis = full | ((kk < Sk) & (!causal | (kk <= qrow + off)) &
+                                         ((window <= 0) | (kk > qrow + off - window)));
+                const float e = exp2_fast(fmaf(st[r], sl2, -lse2));
+                const float p = vis ? e : 0.f;
                 ds[r] = p * (dpt[r] - dsq);
             }
-            const bf16x4 dsb = pack4(ds);                   // dS^T as B operand (k = keys, column = query)
+            bf16x8 kc[2][kNT];
 #pragma unroll
-            for (int t = 0; t < kT; ++t) dqa[t] = mfma16(col_frag<D>(kt, r0, 16 * t, lane), dsb, dqa[t]);
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) kc[s2][t] = col_frag8<D>(kt, r0 + 16 * s2, 32 * t, lane);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 dsb = pack8(ds, s2);           // dS^T as B operand (k = keys, column = query)
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) dqa[t] = mfma32(kc[s2][t], dsb, dqa[t]);
+            }
         }
         if (it + 1 < ntiles) {
             __syncthreads();
@@ -348,11 +462,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     }
     if (qrow < Sq) {
 #pragma unroll
-        for (int t = 0; t < kT; ++t) {
-            const u32x2 w = {pack_bf16x2(dqa[t][0] * scale, dqa[t][1] * scale),
-                             pack_bf16x2(dqa[t][2] * scale, dqa[t][3] * scale)};
-            *reinterpret_cast<u32x2*>(dq + (qbase + qrow) * D + 16 * t + 4 * q4) = w;
-        }
+        for (int t = 0; t < kNT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x2 w = {pack_bf16x2(dqa[t][4 * j + 0] * scale, dqa[t][4 * j + 1] * scale),
+                                 pack_bf16x2(dqa[t][4 * j + 2] * scale, dqa[t][4 * j + 3] * scale)};
+                *reinterpret_cast<u32x2*>(dq + (qbase + qrow) * D + 32 * t + 8 * j + 4 * h) = w;
+            }
     }
 }
 
@@ -368,10 +484,11 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
     if (rows > 0)
         hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows * 16 + kBwdThreads - 1) / kBwdThreads)),
                            dim3(kBwdThreads), 0, stream, o, dout, a.dsum, rows);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((a.Sk + kTileRows - 1) / kTileRows, a.Hkv, a.B),
+    // 1-D grids of (blocks x heads x B) workgroups
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((a.Sk + kBlockRows - 1) / kBlockRows * a.Hkv * a.B),
                        dim3(kBwdThreads), 0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dk),
                        static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, causal, a.window);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((a.Sq + kTileRows - 1) / kTileRows, a.Hq, a.B), dim3(kBwdThreads),
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((a.Sq + kBlockRows - 1) / kBlockRows * a.Hq * a.B), dim3(kBwdThreads),
                        0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.Sq,
                        a.Sk, a.scale, causal, a.window);
     return hipGetLastError();

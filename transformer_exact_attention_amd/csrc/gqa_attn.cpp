@@ -142,6 +142,7 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o,
     if (st != GQA_OK) return st;
     if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * Sq >= ((int64_t)1 << 27)) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)(Sk + 127) / 128 * Hkv * B >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;   // 1-D grid
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GQA_ERR_WORKSPACE;
     if (workspace_bytes < attn_prefill_bwd_workspace_bytes(B, Hq, Sq)) return GQA_ERR_WORKSPACE;
     gqa::BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
