@@ -553,7 +553,7 @@ def main():
         traffic = kernel_traffic("prefill_bf16_gqa_causal_B2_Hq32_Hkv8_S8192", src_prefill)
         out["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                           "kernel": "prefill_bf16_kernel<128>",
+                           "kernel": "prefill_bf16_kernel<128, false>",
                            "algorithmic_flops_per_launch": wp.flops(),
                            "algorithmic_bytes_per_launch": wp.io_bytes(),
                            "avg_launch_us": round(t * 1e6, 2), "min_launch_us": round(float(np.min(res["prefill"])) * 1e6, 2)}
