@@ -13,21 +13,18 @@
 //
 // Three kernels, no atomics:
 //   * rowdot: D for every query row;
-//   * dkdv: a workgroup owns 64 keys of one K/V head (a wavefront 16 of
-//     them) and walks every query tile of the group's g heads, keeping dK and
-//     dV in registers;
-//   * dq: a workgroup owns 64 query rows of one head (a wavefront 16) and
-//     walks the key tiles, keeping dQ^T in registers.
-// Products are v_mfma_f32_16x16x16_bf16 (A: lane (c, q4) holds row c,
-// k = 4 q4..4 q4+3; B: k = 4 q4..+3 of column c; D: rows 4 q4..+3 of column c,
-// with c = lane % 16, q4 = lane / 16).  Tiles of 64 rows are staged in LDS
-// with rows padded to D*2 + 16 bytes (row reads of 16 lanes hit distinct
-// banks); column operands come from transposing LDS reads
-// (ds_read_b64_tr_b16: lane r of a 16-lane group addressing row r/4,
-// columns 4 (r%4).. delivers to lane l the four rows of column l).
-// Each product computed in D layout is already the A or B layout of the
-// product that consumes it: P (rows q, columns keys) is P^T's A layout, and
-// dS^T (rows keys, columns q) is dQ^T's B layout.
+//   * dkdv: a workgroup of 4 wavefronts owns 128 keys of one K/V head (a
+//     wavefront 32 of them) and walks every query tile of the group's g
+//     heads, keeping dK and dV in registers;
+//   * dq: a workgroup of 8 wavefronts owns 256 query rows of one head (a
+//     wavefront 32) and walks the key tiles, keeping dQ^T in registers.
+// Products are v_mfma_f32_32x32x16_bf16.  Each product computed in the
+// accumulator layout is already an operand of the product that consumes it:
+// P and dS (rows q, columns keys) are the A operands of dV = P^T dO and
+// dK = dS^T Q, and dS^T (rows keys, columns q) is the B operand of
+// dQ^T = K^T dS^T.  Tiles of 64 rows are staged in LDS with XOR-swizzled
+// 16-byte units, so row reads and transposing column reads
+// (ds_read_b64_tr_b16) are both conflict-free.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -72,24 +69,24 @@ struct Tile {
 // callers multiply by a zero probability); the loads stay unconditional, so
 // no branch keeps the compiler from overlapping them with the tile's work.
 // 256 threads, 16-byte chunks.
-template <int D>
-__device__ __forceinline__ void load_rows(u32x4 (&reg)[kTileRows * D / 8 / kBwdThreads], const uint16_t* base,
+template <int D, int NT = kBwdThreads>
+__device__ __forceinline__ void load_rows(u32x4 (&reg)[kTileRows * D / 8 / NT], const uint16_t* base,
                                           int row0, int rows_total) {
     constexpr int kChunks = D / 8;
 #pragma unroll
-    for (int x = 0; x < kTileRows * kChunks / kBwdThreads; ++x) {
-        const int i = x * kBwdThreads + (int)threadIdx.x;
+    for (int x = 0; x < kTileRows * kChunks / NT; ++x) {
+        const int i = x * NT + (int)threadIdx.x;
         const int r = i / kChunks, c = i % kChunks;
         const int row = min(row0 + r, rows_total - 1);
         reg[x] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + 8 * c);
     }
 }
-template <int D>
-__device__ __forceinline__ void store_rows(lds_char* tile, const u32x4 (&reg)[kTileRows * D / 8 / kBwdThreads]) {
+template <int D, int NT = kBwdThreads>
+__device__ __forceinline__ void store_rows(lds_char* tile, const u32x4 (&reg)[kTileRows * D / 8 / NT]) {
     constexpr int kChunks = D / 8;
 #pragma unroll
-    for (int x = 0; x < kTileRows * kChunks / kBwdThreads; ++x) {
-        const int i = x * kBwdThreads + (int)threadIdx.x;
+    for (int x = 0; x < kTileRows * kChunks / NT; ++x) {
+        const int i = x * NT + (int)threadIdx.x;
         const int r = i / kChunks, c = i % kChunks;
         *(lds_u32x4*)(tile + Tile<D>::off(r, 8 * c)) = reg[x];
     }
@@ -327,16 +324,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         }
 }
 
-// dQ for 128 query rows of head hq of batch b (32 per wavefront).  Key tiles
+// dQ for 256 query rows of head hq of batch b (32 per wavefront).  Key tiles
 // of 64 keys stream through LDS.
+// Eight wavefronts (two per SIMD, 230 registers each) share every staged
+// K/V tile: half the tile bytes per FLOP of four, and a second wavefront on
+// each SIMD to cover latency.  (The dK/dV kernel keeps four: it needs about
+// 390 registers per wavefront.)
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqBlockRows = kDqWaves * kWaveRows;
+
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int Hq, int Hkv, int Sq, int Sk, float scale, int causal, int window) {
     constexpr int kT = D / 16;
     constexpr int kNT = D / 32;
-    constexpr int kRegs = kTileRows * D / 8 / kBwdThreads;
+    constexpr int kRegs = kTileRows * D / 8 / kDqThreads;
     __shared__ __attribute__((aligned(16))) char k_raw[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char v_raw[2][Tile<D>::kBytes];
 
@@ -345,14 +350,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     // 1-D grid, query block slowest; causal: the last query blocks see the
     // most keys, so they start first.  The heads of a group are adjacent
     // (their shared K/V tiles meet in cache).
-    const int nqb = (Sq + kBlockRows - 1) / kBlockRows;
+    const int nqb = (Sq + kDqBlockRows - 1) / kDqBlockRows;
     const int planes = (int)gridDim.x / nqb;                                      // Hq * B
     const int rank = (int)blockIdx.x / planes;
     const int qb = causal ? nqb - 1 - rank : rank;
     const int hq = (int)blockIdx.x % Hq, b = ((int)blockIdx.x % planes) / Hq;
     const int g = Hq / Hkv, hk = hq / g;
     const int off = Sk - Sq;
-    const int qw0 = qb * kBlockRows + kWaveRows * wave;    // this wavefront's rows qw0 .. qw0 + 31
+    const int qw0 = qb * kDqBlockRows + kWaveRows * wave;    // this wavefront's rows qw0 .. qw0 + 31
     const int qrow = qw0 + n;                              // this lane's query column
     const float sl2 = scale * kLog2e;
     const size_t qbase = ((size_t)b * Hq + hq) * Sq;
@@ -383,19 +388,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 
     // Key tiles seen by the block's rows (causal: keys <= row + off; window W:
     // also keys > row + off - W).
-    const int q_last = min(qb * kBlockRows + kBlockRows, Sq) - 1;
+    const int q_last = min(qb * kDqBlockRows + kDqBlockRows, Sq) - 1;
     const int kend = causal ? min(Sk, q_last + off + 1) : Sk;
-    const int kfirst = window > 0 ? max(0, qb * kBlockRows + off - window + 1) / kTileRows : 0;
+    const int kfirst = window > 0 ? max(0, qb * kDqBlockRows + off - window + 1) / kTileRows : 0;
     const int ntiles = max(0, (kend + kTileRows - 1) / kTileRows - kfirst);
     const size_t kvbase = ((size_t)b * Hkv + hk) * Sk;
     u32x4 kr[kRegs], vr[kRegs];
     auto fetch = [&](int i) {
-        load_rows<D>(kr, k + kvbase * D, (kfirst + i) * kTileRows, Sk);
-        load_rows<D>(vr, v + kvbase * D, (kfirst + i) * kTileRows, Sk);
+        load_rows<D, kDqThreads>(kr, k + kvbase * D, (kfirst + i) * kTileRows, Sk);
+        load_rows<D, kDqThreads>(vr, v + kvbase * D, (kfirst + i) * kTileRows, Sk);
     };
     auto stash = [&](int buf) {
-        store_rows<D>((lds_char*)k_raw[buf], kr);
-        store_rows<D>((lds_char*)v_raw[buf], vr);
+        store_rows<D, kDqThreads>((lds_char*)k_raw[buf], kr);
+        store_rows<D, kDqThreads>((lds_char*)v_raw[buf], vr);
     };
     if (ntiles > 0) {
         fetch(0);
@@ -488,7 +493,7 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((a.Sk + kBlockRows - 1) / kBlockRows * a.Hkv * a.B),
                        dim3(kBwdThreads), 0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dk),
                        static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, causal, a.window);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((a.Sq + kBlockRows - 1) / kBlockRows * a.Hq * a.B), dim3(kBwdThreads),
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((a.Sq + kDqBlockRows - 1) / kDqBlockRows * a.Hq * a.B), dim3(kDqThreads),
                        0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.Sq,
                        a.Sk, a.scale, causal, a.window);
     return hipGetLastError();
