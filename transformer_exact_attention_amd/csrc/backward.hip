@@ -13,18 +13,22 @@
 //
 // Three kernels, no atomics:
 //   * rowdot: D for every query row;
-//   * dkdv: a workgroup of 4 wavefronts owns 128 keys of one K/V head (a
-//     wavefront 32 of them) and walks every query tile of the group's g
-//     heads, keeping dK and dV in registers;
+//   * dkdv: a workgroup of 8 wavefronts owns 256 keys of one K/V head (a
+//     wavefront 32 of them, their K rows in registers, the V rows of all 256
+//     in LDS) and walks every 64-row query tile of the group's g heads,
+//     keeping dK and dV in registers;
 //   * dq: a workgroup of 8 wavefronts owns 256 query rows of one head (a
-//     wavefront 32) and walks the key tiles, keeping dQ^T in registers.
+//     wavefront 32) and walks the 64-key tiles, keeping dQ^T in registers.
+// Eight wavefronts share every staged tile (half the tile bytes per FLOP of
+// four) and two share each SIMD; keeping V in LDS is what fits a dK/dV
+// wavefront in 256 registers.
 // Products are v_mfma_f32_32x32x16_bf16.  Each product computed in the
 // accumulator layout is already an operand of the product that consumes it:
 // P and dS (rows q, columns keys) are the A operands of dV = P^T dO and
 // dK = dS^T Q, and dS^T (rows keys, columns q) is the B operand of
-// dQ^T = K^T dS^T.  Tiles of 64 rows are staged in LDS with XOR-swizzled
-// 16-byte units, so row reads and transposing column reads
-// (ds_read_b64_tr_b16) are both conflict-free.
+// dQ^T = K^T dS^T.  Tiles are staged in LDS with XOR-swizzled 16-byte units
+// (D = 128), so row reads and transposing column reads (ds_read_b64_tr_b16)
+// are both conflict-free.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -151,55 +155,70 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int s) {
 }
 
 constexpr int kWaveRows = 32;                      // keys (dK/dV) or query rows (dQ) per wavefront
-constexpr int kBlockRows = 4 * kWaveRows;          // per workgroup
 
-// dK, dV for 128 keys of K/V head hk of batch b (32 per wavefront).  Query
+// dK, dV for 256 keys of K/V head hk of batch b (32 per wavefront).  Query
 // tiles of 64 rows of every head of the group stream through LDS.
+constexpr int kDkWaves = 8;
+constexpr int kDkThreads = 64 * kDkWaves;
+constexpr int kDkBlockRows = kDkWaves * kWaveRows;
+
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int Sq, int Sk, float scale,
     int causal, int window) {
     constexpr int kT = D / 16;                             // 16-wide d steps
     constexpr int kNT = D / 32;                            // 32-wide d tiles of dK, dV
-    constexpr int kRegs = kTileRows * D / 8 / kBwdThreads;
+    constexpr int kRegs = kTileRows * D / 8 / kDkThreads;
     __shared__ __attribute__((aligned(16))) char q_raw[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char d_raw[2][Tile<D>::kBytes];
     __shared__ float2 row_s[2][kTileRows];                 // (lse * log2 e, D) per row
+    __shared__ __attribute__((aligned(16))) char v_all[kDkBlockRows * Tile<D>::kRowBytes];   // V rows of the block's keys
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     // 1-D grid, key block slowest: under a causal mask the first key blocks
     // see the most query rows, so the heaviest workgroups start first
-    const int planes = (int)gridDim.x / ((Sk + kBlockRows - 1) / kBlockRows);     // Hkv * B
+    const int planes = (int)gridDim.x / ((Sk + kDkBlockRows - 1) / kDkBlockRows);     // Hkv * B
     const int kb = (int)blockIdx.x / planes, hk = (int)blockIdx.x % Hkv, b = ((int)blockIdx.x % planes) / Hkv;
     const int g = Hq / Hkv;
     const int off = Sk - Sq;
-    const int kw0 = kb * kBlockRows + kWaveRows * wave;    // this wavefront's keys kw0 .. kw0 + 31
+    const int kw0 = kb * kDkBlockRows + kWaveRows * wave;    // this wavefront's keys kw0 .. kw0 + 31
     const int key = kw0 + n;                               // this lane's key column
     const float sl2 = scale * kLog2e;
 
     // K and V rows of the wavefront's keys as B operands (k = d, column = key).
-    bf16x8 kf[kT], vf[kT];
+    // K rows of the wavefront's keys as B operands (k = d, column = key) in
+    // registers; the V rows of all the workgroup's keys in LDS (read as the
+    // same B operand each sub-step), which keeps a wavefront within 256
+    // registers so two share each SIMD.
+    bf16x8 kf[kT];
     {
         const size_t kvrow = ((size_t)b * Hkv + hk) * Sk;
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
-            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-            if (key < Sk) {
-                kw = *reinterpret_cast<const u32x4*>(k + (kvrow + key) * D + 16 * t + 8 * h);
-                vw = *reinterpret_cast<const u32x4*>(v + (kvrow + key) * D + 16 * t + 8 * h);
-            }
+            u32x4 kw = {0u, 0u, 0u, 0u};
+            if (key < Sk) kw = *reinterpret_cast<const u32x4*>(k + (kvrow + key) * D + 16 * t + 8 * h);
             kf[t] = __builtin_bit_cast(bf16x8, kw);
-            vf[t] = __builtin_bit_cast(bf16x8, vw);
+        }
+        constexpr int kVChunks = kDkBlockRows * D / 8 / kDkThreads;
+#pragma unroll
+        for (int x = 0; x < kVChunks; ++x) {
+            const int i = x * kDkThreads + (int)threadIdx.x;
+            const int r = i / (D / 8), c = i % (D / 8);
+            const int row = min(kb * kDkBlockRows + r, Sk - 1);
+            *(lds_u32x4*)((lds_char*)v_all + Tile<D>::off(r, 8 * c)) =
+                *reinterpret_cast<const u32x4*>(v + (kvrow + row) * D + 8 * c);
         }
         // Redefine the fragments past their loads: the loop below then sees
         // registers with no load pending and never waits on the tile
         // prefetches it has in flight (the wait counter is in order).
 #pragma unroll
-        for (int t = 0; t < kT; ++t) asm volatile("" : "+v"(kf[t]), "+v"(vf[t]));
+        for (int t = 0; t < kT; ++t) asm volatile("" : "+v"(kf[t]));
     }
+    const lds_char* const vrow = (const lds_char*)v_all;
+    const int vr = kWaveRows * wave + n;                   // this lane's key row in v_all
     f32x16 dka[kNT], dva[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
@@ -209,10 +228,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     // Query tiles: for each head of the group, the tiles holding a row that
     // sees one of the workgroup's keys (causal: rows i >= key - off; window W:
     // also i < key - off + W).
-    const int first_tile = causal ? max(0, kb * kBlockRows - off) / kTileRows : 0;
+    const int first_tile = causal ? max(0, kb * kDkBlockRows - off) / kTileRows : 0;
     int end_tile = (Sq + kTileRows - 1) / kTileRows;
     if (window > 0)
-        end_tile = min(end_tile, max(0, kb * kBlockRows + kBlockRows - 1 - off + window - 1) / kTileRows + 1);
+        end_tile = min(end_tile, max(0, kb * kDkBlockRows + kDkBlockRows - 1 - off + window - 1) / kTileRows + 1);
     const int n_per_head = max(0, end_tile - first_tile);
     const int total = g * n_per_head;
     u32x4 qr[kRegs], dr[kRegs];
@@ -220,15 +239,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         const int hq = hk * g + it / n_per_head;
         const int row0 = (first_tile + it % n_per_head) * kTileRows;
         const size_t base = ((size_t)b * Hq + hq) * Sq;
-        load_rows<D>(qr, q + base * D, row0, Sq);
-        load_rows<D>(dr, dout + base * D, row0, Sq);
+        load_rows<D, kDkThreads>(qr, q + base * D, row0, Sq);
+        load_rows<D, kDkThreads>(dr, dout + base * D, row0, Sq);
     };
     auto stash = [&](int it, int buf) {
         const int hq = hk * g + it / n_per_head;
         const int row0 = (first_tile + it % n_per_head) * kTileRows;
         const size_t base = ((size_t)b * Hq + hq) * Sq;
-        store_rows<D>((lds_char*)q_raw[buf], qr);
-        store_rows<D>((lds_char*)d_raw[buf], dr);
+        store_rows<D, kDkThreads>((lds_char*)q_raw[buf], qr);
+        store_rows<D, kDkThreads>((lds_char*)d_raw[buf], dr);
         if (threadIdx.x < kTileRows) {
             const int row = row0 + threadIdx.x;
             // rows past Sq: lse = +inf makes their probabilities 0
@@ -258,16 +277,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
             f32x16 sc, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
-            bf16x8 qa[kT], da[kT];                          // all operand reads first, one wait
 #pragma unroll
             for (int t = 0; t < kT; ++t) {
-                qa[t] = row_frag8<D>(qt, r0 + n, 16 * t + 8 * h);
-                da[t] = row_frag8<D>(dt, r0 + n, 16 * t + 8 * h);
-            }
-#pragma unroll
-            for (int t = 0; t < kT; ++t) {
-                sc = mfma32(qa[t], kf[t], sc);
-                dp = mfma32(da[t], vf[t], dp);
+                sc = mfma32(row_frag8<D>(qt, r0 + n, 16 * t + 8 * h), kf[t], sc);
+                dp = mfma32(row_frag8<D>(dt, r0 + n, 16 * t + 8 * h), row_frag8<D>(vrow, vr, 16 * t + 8 * h), dp);
             }
             // every (row, key) of the block visible?
             const bool full = (!causal || pos0 + off >= kw0 + kWaveRows - 1) &&
@@ -284,21 +297,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
                 p[r] = vis ? e : 0.f;
                 ds[r] = p[r] * (dp[r] - ld.y);
             }
-            bf16x8 dc[2][kNT], qc[2][kNT];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int t = 0; t < kNT; ++t) {
-                    dc[s2][t] = col_frag8<D>(dt, r0 + 16 * s2, 32 * t, lane);
-                    qc[s2][t] = col_frag8<D>(qt, r0 + 16 * s2, 32 * t, lane);
-                }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const bf16x8 pa = pack8(p, s2), dsa = pack8(ds, s2);   // P^T, dS^T as A (rows = keys)
 #pragma unroll
                 for (int t = 0; t < kNT; ++t) {
-                    dva[t] = mfma32(pa, dc[s2][t], dva[t]);
-                    dka[t] = mfma32(dsa, qc[s2][t], dka[t]);
+                    dva[t] = mfma32(pa, col_frag8<D>(dt, r0 + 16 * s2, 32 * t, lane), dva[t]);
+                    dka[t] = mfma32(dsa, col_frag8<D>(qt, r0 + 16 * s2, 32 * t, lane), dka[t]);
                 }
             }
         }
@@ -326,10 +331,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
 
 // dQ for 256 query rows of head hq of batch b (32 per wavefront).  Key tiles
 // of 64 keys stream through LDS.
-// Eight wavefronts (two per SIMD, 230 registers each) share every staged
-// K/V tile: half the tile bytes per FLOP of four, and a second wavefront on
-// each SIMD to cover latency.  (The dK/dV kernel keeps four: it needs about
-// 390 registers per wavefront.)
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqBlockRows = kDqWaves * kWaveRows;
@@ -490,8 +491,8 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows * 16 + kBwdThreads - 1) / kBwdThreads)),
                            dim3(kBwdThreads), 0, stream, o, dout, a.dsum, rows);
     // 1-D grids of (blocks x heads x B) workgroups
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((a.Sk + kBlockRows - 1) / kBlockRows * a.Hkv * a.B),
-                       dim3(kBwdThreads), 0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dk),
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((a.Sk + kDkBlockRows - 1) / kDkBlockRows * a.Hkv * a.B),
+                       dim3(kDkThreads), 0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dk),
                        static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, causal, a.window);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((a.Sq + kDqBlockRows - 1) / kDqBlockRows * a.Hq * a.B), dim3(kDqThreads),
                        0, stream, q, k, v, dout, a.lse, a.dsum, static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.Sq,
