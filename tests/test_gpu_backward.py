@@ -107,6 +107,9 @@ CASES = [
     (128, 1, 2, 1, 1, 1, False, 0),          # one query, one key
     (64, 1, 4, 2, 5, 70, True, 0),           # fewer queries than a tile
     (128, 1, 4, 4, 64, 64, True, 1),         # one-key window: dq = dk = 0, dv = dO
+    (64, 2, 4, 2, 300, 100, False, 0),       # non-causal with more queries than keys
+    (128, 1, 128, 1, 40, 300, True, 0),      # g = 128 (every query head reads one K/V head)
+    (128, 1, 8, 2, 513, 700, True, 300),     # window with Sq < Sk, several 256-row blocks
 ]
 
 
