@@ -188,7 +188,6 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
     const int key = kw0 + n;                               // this lane's key column
     const float sl2 = scale * kLog2e;
 
-    // K and V rows of the wavefront's keys as B operands (k = d, column = key).
     // K rows of the wavefront's keys as B operands (k = d, column = key) in
     // registers; the V rows of all the workgroup's keys in LDS (read as the
     // same B operand each sub-step), which keeps a wavefront within 256
