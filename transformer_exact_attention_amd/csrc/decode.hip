@@ -478,10 +478,12 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
 // owns d = 2*lane, 2*lane+1.  Wavefront w merges partials w, w + kCombineWaves,
 // ... in one pass with a running maximum (the rescale step of the tiled
 // online softmax), issuing the loads of several partials at once; the
-// wavefronts' results are then merged in LDS in a fixed order.
-constexpr int kCombineWaves = 4;
+// wavefronts' results are then merged in LDS in a fixed order.  With few
+// partials per row (short caches) one wavefront per row does it all.
 constexpr int kCombineBatch = 4;         // partials in flight per wavefront
+constexpr int kCombineFewPartials = 32;  // at most this many per row: one wavefront
 
+template <int kCombineWaves>
 __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ lsepart, const long long* __restrict__ prefix,
     uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW) {
@@ -569,8 +571,12 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
                        a.scale * kLog2e, a.window > 0 ? a.window : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(64 * kCombineWaves), 0, stream, opart, lsepart, prefix,
-                       static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
+    if (P <= kCombineFewPartials)
+        hipLaunchKernelGGL(decode_combine_kernel<1>, dim3(a.Hq, a.B), dim3(64), 0, stream, opart, lsepart, prefix,
+                           static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
+    else
+        hipLaunchKernelGGL(decode_combine_kernel<4>, dim3(a.Hq, a.B), dim3(256), 0, stream, opart, lsepart, prefix,
+                           static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
     return hipGetLastError();
 }
 
