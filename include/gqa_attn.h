@@ -126,17 +126,18 @@ size_t attn_prefill_bwd_workspace_bytes(int B, int Hq, int Sq);
  *   dq = scale dS k,  dk = scale dS^T q,
  * and a K/V head's dk, dv sum over the g query heads that read it.
  *
- *   q, o, dout, dq : [B, Hq, Sq, d]     k, v, dk, dv : [B, Hkv, Sk, d]   (bf16)
+ *   q, o, dout, dq : [B, Hq, Sq, d]     k, v, dk, dv : [B, Hkv, Sk, d]   (dtype)
  *   lse            : fp32 [B, Hq, Sq] from attn_prefill_lse_fwd with the same
  *                    q, k, v, scale, causal and window
  *   workspace      : device, >= attn_prefill_bwd_workspace_bytes(B, Hq, Sq)
  *                    bytes, 256-byte aligned; contents on entry are ignored.
  * dq, dk, dv are overwritten (not accumulated into) and must not overlap any
- * input.  Supported: GQA_BF16, d in {64, 128}, B * Hq * Sq < 2^27,
- * ceil(Sk / 128) * Hkv * B < 2^31, group
- * sizes as attn_prefill_fwd.  GQA_ERR_INVALID_ARG as attn_prefill_lse_fwd
- * and for NULL dout/dq/dk/dv; GQA_ERR_UNSUPPORTED for GQA_F32;
- * GQA_ERR_WORKSPACE for a short, NULL or misaligned workspace.
+ * input.  Supported: d in {64, 128}, B * Hq * Sq < 2^27,
+ * ceil(Sk / 128) * Hkv * B < 2^31, group sizes as attn_prefill_fwd; GQA_BF16
+ * (matrix cores) and GQA_F32 (all tensors fp32; vector-ALU kernels, one
+ * wavefront per row, meant for small problems).  GQA_ERR_INVALID_ARG as
+ * attn_prefill_lse_fwd and for NULL dout/dq/dk/dv; GQA_ERR_WORKSPACE for a
+ * short, NULL or misaligned workspace.
  */
 int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,

@@ -193,7 +193,7 @@ def bwd(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
     (dict(dv=None), 1), (dict(k=None), 1), (dict(window=-2), 1), (dict(Sq=32, Sk=16), 1), (dict(Hq=6, Hkv=4), 1),
-    (dict(scale=0.0), 1), (dict(dtype=0), 2), (dict(d=96), 2), (dict(B=2048, Hq=128, Hkv=128, Sq=1024, Sk=1024), 2),
+    (dict(scale=0.0), 1), (dict(dtype=5), 1), (dict(d=96), 2), (dict(B=2048, Hq=128, Hkv=128, Sq=1024, Sk=1024), 2),
     (dict(ws=None), 3), (dict(ws=0x100000 * 256 + 64), 3), (dict(ws_bytes=16 * 4 * 4 - 4), 3),
 ])
 def test_prefill_bwd_rejects_on_host(lib, kw, status):

@@ -132,6 +132,37 @@ def test_backward_matches_oracle(ga, d, B, Hq, Hkv, Sq, Sk, causal, Wn):
         assert np.array_equal(to_f64(dv), ref_f64(do, "bf16"))
 
 
+# fp32: each term carries a relative error of a few fp32 units (the lse of
+# the fp32 forward is exact to about 1e-6); 2^-14 of the term magnitudes
+# leaves a wide margin over sums of a few thousand terms.
+F32_TERM_TOL = 2.0 ** -14
+
+
+@pytest.mark.parametrize("d,B,Hq,Hkv,Sq,Sk,causal,Wn", [
+    (64, 1, 4, 2, 128, 128, True, 0),        # the tiny fp32 workload's shape, causal
+    (128, 2, 4, 4, 70, 150, False, 0),       # MHA, non-causal, Sq < Sk
+    (64, 1, 8, 1, 100, 100, True, 17),       # MQA with a window
+])
+def test_backward_f32_matches_oracle(ga, d, B, Hq, Hkv, Sq, Sk, causal, Wn):
+    import torch
+    note(f"backward f32 d{d} B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} causal={causal} W{Wn}")
+    q, k, v = inputs(120 + Sq, B, Hq, Hkv, Sq, Sk, d, "f32")
+    do = W.normal([121 + Sq, 3], (B, Hq, Sq, d), "f32")
+    qg, kg, vg, dog = (to_gpu(x, "f32") for x in (q, k, v, do))
+    o, lse = ga.attn_prefill_lse_fwd(qg, kg, vg, causal=causal, window=Wn)
+    grads = ga.attn_prefill_bwd(qg, kg, vg, o, lse, dog, causal=causal, window=Wn)
+    torch.cuda.synchronize()
+    args = tuple(np.asarray(x, np.float64) for x in (q, k, v, do))
+    refs = oracle.attention_backward(*args, causal=causal, window=Wn or None)
+    mags = oracle.gradient_magnitudes(*args, causal=causal, window=Wn or None)
+    for got, ref, mag, name in zip(grads, refs, mags, ("dq", "dk", "dv")):
+        got = to_f64(got)
+        assert np.all(np.isfinite(got)), name
+        err = np.abs(got - ref)
+        worst = float((err / (F32_TERM_TOL * mag + 1e-30)).max())
+        assert worst <= 1.0, f"{name}: error reaches {worst:.2f} x its bound (max abs err {err.max():.3e})"
+
+
 def test_backward_scale_and_outputs_overwritten(ga):
     """A non-default scale, and dq/dk/dv buffers holding garbage on entry."""
     import torch

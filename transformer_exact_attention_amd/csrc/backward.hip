@@ -499,11 +499,163 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// fp32 backward on the vector ALU (the fp32 forward's counterpart, for
+// small problems): one wavefront per row, lane l holding elements
+// l, l + 64, ... of it; dot products reduce across the wavefront.
+constexpr int kF32Waves = 4;
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// D = rowsum(dO * O) per query row.
+template <int D>
+__global__ __launch_bounds__(64 * kF32Waves) void bwd_f32_rowdot_kernel(const float* __restrict__ o,
+                                                                        const float* __restrict__ dout,
+                                                                        float* __restrict__ dsum, long long rows) {
+    constexpr int E = D / 64;
+    const long long row = (long long)blockIdx.x * kF32Waves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;                               // whole wavefronts leave together
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf(o[row * D + lane + 64 * e], dout[row * D + lane + 64 * e], acc);
+    acc = wave_sum(acc);
+    if (lane == 0) dsum[row] = acc;
+}
+
+// dQ of one query row: sum over its visible keys j of dS_ij k_j.
+template <int D>
+__global__ __launch_bounds__(64 * kF32Waves) void bwd_f32_dq_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
+    float* __restrict__ dq, int Hq, int Hkv, int Sq, int Sk, float scale, int causal, int window, long long rows) {
+    constexpr int E = D / 64;
+    const long long row = (long long)blockIdx.x * kF32Waves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int i = (int)(row % Sq);
+    const long long bh = row / Sq;                         // b * Hq + h
+    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+    const int hk = h / (Hq / Hkv);
+    const int off = Sk - Sq;
+    const float sl2 = scale * kLog2e, l2 = lse[row] * kLog2e, dd = dsum[row];
+    float qv[E], ov[E], acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        qv[e] = q[row * D + lane + 64 * e];
+        ov[e] = dout[row * D + lane + 64 * e];
+        acc[e] = 0.f;
+    }
+    const int jend = causal ? min(Sk, i + off + 1) : Sk;
+    const int jbeg = window > 0 ? max(0, i + off - window + 1) : 0;
+    const float* kb = k + ((size_t)b * Hkv + hk) * Sk * D;
+    const float* vb = v + ((size_t)b * Hkv + hk) * Sk * D;
+    for (int j = jbeg; j < jend; ++j) {
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            s = fmaf(qv[e], kb[(size_t)j * D + lane + 64 * e], s);
+            dp = fmaf(ov[e], vb[(size_t)j * D + lane + 64 * e], dp);
+        }
+        s = wave_sum(s);
+        dp = wave_sum(dp);
+        const float ds = exp2_fast(fmaf(s, sl2, -l2)) * (dp - dd);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kb[(size_t)j * D + lane + 64 * e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) dq[row * D + lane + 64 * e] = acc[e] * scale;
+}
+
+// dK, dV of one key row: sums over the visible rows i of the g query heads
+// reading it of dS_ij q_i and P_ij dO_i.
+template <int D>
+__global__ __launch_bounds__(64 * kF32Waves) void bwd_f32_dkdv_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
+    float* __restrict__ dk, float* __restrict__ dv, int Hq, int Hkv, int Sq, int Sk, float scale, int causal,
+    int window, long long rows) {
+    constexpr int E = D / 64;
+    const long long row = (long long)blockIdx.x * kF32Waves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int j = (int)(row % Sk);
+    const long long bh = row / Sk;                         // b * Hkv + hk
+    const int hk = (int)(bh % Hkv), b = (int)(bh / Hkv);
+    const int g = Hq / Hkv;
+    const int off = Sk - Sq;
+    const float sl2 = scale * kLog2e;
+    float kv[E], vv[E], ak[E], av[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kv[e] = k[row * D + lane + 64 * e];
+        vv[e] = v[row * D + lane + 64 * e];
+        ak[e] = av[e] = 0.f;
+    }
+    // rows i that see key j: i >= j - off (causal), i < j - off + W (window)
+    const int ibeg = causal ? max(0, j - off) : 0;
+    const int iend = window > 0 ? min(Sq, j - off + window) : Sq;
+    for (int hh = 0; hh < g; ++hh) {
+        const size_t base = ((size_t)b * Hq + (size_t)hk * g + hh) * Sq;
+        for (int i = ibeg; i < iend; ++i) {
+            const float* qi = q + (base + i) * D;
+            const float* oi = dout + (base + i) * D;
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                s = fmaf(qi[lane + 64 * e], kv[e], s);
+                dp = fmaf(oi[lane + 64 * e], vv[e], dp);
+            }
+            s = wave_sum(s);
+            dp = wave_sum(dp);
+            const float p = exp2_fast(fmaf(s, sl2, -lse[base + i] * kLog2e));
+            const float ds = p * (dp - dsum[base + i]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                av[e] = fmaf(p, oi[lane + 64 * e], av[e]);
+                ak[e] = fmaf(ds, qi[lane + 64 * e], ak[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        dk[row * D + lane + 64 * e] = ak[e] * scale;
+        dv[row * D + lane + 64 * e] = av[e];
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_f32(const BackwardArgs& a, hipStream_t stream) {
+    const float* q = static_cast<const float*>(a.q);
+    const float* k = static_cast<const float*>(a.k);
+    const float* v = static_cast<const float*>(a.v);
+    const float* dout = static_cast<const float*>(a.dout);
+    const long long qrows = (long long)a.B * a.Hq * a.Sq, krows = (long long)a.B * a.Hkv * a.Sk;
+    const int causal = a.causal != 0 || a.window > 0 ? 1 : 0;
+    const dim3 blk(64 * kF32Waves);
+    hipLaunchKernelGGL(bwd_f32_rowdot_kernel<D>, dim3((unsigned)((qrows + kF32Waves - 1) / kF32Waves)), blk, 0,
+                       stream, static_cast<const float*>(a.o), dout, a.dsum, qrows);
+    hipLaunchKernelGGL(bwd_f32_dq_kernel<D>, dim3((unsigned)((qrows + kF32Waves - 1) / kF32Waves)), blk, 0, stream,
+                       q, k, v, dout, a.lse, a.dsum, static_cast<float*>(a.dq), a.Hq, a.Hkv, a.Sq, a.Sk, a.scale,
+                       causal, a.window, qrows);
+    hipLaunchKernelGGL(bwd_f32_dkdv_kernel<D>, dim3((unsigned)((krows + kF32Waves - 1) / kF32Waves)), blk, 0,
+                       stream, q, k, v, dout, a.lse, a.dsum, static_cast<float*>(a.dk), static_cast<float*>(a.dv),
+                       a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, causal, a.window, krows);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Sizes are validated by the caller: B, Hq, Hkv, Sq, Sk > 0, d in {64, 128}.
 hipError_t launch_prefill_bwd_bf16(const BackwardArgs& a, hipStream_t stream) {
     return a.d == 64 ? launch_bwd<64>(a, stream) : launch_bwd<128>(a, stream);
+}
+
+hipError_t launch_prefill_bwd_f32(const BackwardArgs& a, hipStream_t stream) {
+    return a.d == 64 ? launch_bwd_f32<64>(a, stream) : launch_bwd_f32<128>(a, stream);
 }
 
 }  // namespace gqa

@@ -140,14 +140,14 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o,
     // o only marks the output argument of the shared check; q, k, v are read.
     const int st = prefill_check(q, k, v, dq, B, Hq, Hkv, Sq, Sk, d, scale, causal_eff, dtype);
     if (st != GQA_OK) return st;
-    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * Sq >= ((int64_t)1 << 27)) return GQA_ERR_UNSUPPORTED;
     if ((int64_t)(Sk + 127) / 128 * Hkv * B >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;   // 1-D grid
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GQA_ERR_WORKSPACE;
     if (workspace_bytes < attn_prefill_bwd_workspace_bytes(B, Hq, Sq)) return GQA_ERR_WORKSPACE;
     gqa::BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
                         B, Hq, Hkv, Sq, Sk, d, scale, causal_eff, window};
-    const hipError_t e = gqa::launch_prefill_bwd_bf16(a, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == GQA_F32 ? gqa::launch_prefill_bwd_f32(a, s) : gqa::launch_prefill_bwd_bf16(a, s);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 

@@ -120,5 +120,6 @@ hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_copy_blocks(const KvCopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_fp8(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bwd_bf16(const BackwardArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bwd_f32(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace gqa
