@@ -285,16 +285,25 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
             const bool full = (!causal || pos0 + off >= kw0 + kWaveRows - 1) &&
                               (window <= 0 || pos0 + kWaveRows - 1 + off - window < kw0);
             f32x16 p, ds;
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const float2 ld = row_s[buf][qi];
-                const int pos = row0 + qi;
-                // branch-free (a branch would split the scheduling region)
-                const bool vis = full | ((!causal | (key <= pos + off)) & ((window <= 0) | (key > pos + off - window)));
-                const float e = exp2_fast(fmaf(sc[r], sl2, -ld.x));
-                p[r] = vis ? e : 0.f;
-                ds[r] = p[r] * (dp[r] - ld.y);
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float2 ld = row_s[buf][qi];
+                    p[r] = exp2_fast(fmaf(sc[r], sl2, -ld.x));
+                    ds[r] = p[r] * (dp[r] - ld.y);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float2 ld = row_s[buf][qi];
+                    const int pos = row0 + qi;
+                    const bool vis = (!causal | (key <= pos + off)) & ((window <= 0) | (key > pos + off - window));
+                    const float e = exp2_fast(fmaf(sc[r], sl2, -ld.x));
+                    p[r] = vis ? e : 0.f;
+                    ds[r] = p[r] * (dp[r] - ld.y);
+                }
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -438,14 +447,17 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(
             const bool full = key0 + kWaveRows - 1 < Sk && (!causal || key0 + kWaveRows - 1 <= qw0 + off) &&
                               (window <= 0 || key0 > qw0 + kWaveRows - 1 + off - window);
             f32x16 ds;
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool vis = full | ((kk < Sk) & (!causal | (kk <= qrow + off)) &
-                                         ((window <= 0) | (kk > qrow + off - window)));
-                const float e = exp2_fast(fmaf(st[r], sl2, -lse2));
-                const float p = vis ? e : 0.f;
-                ds[r] = p * (dpt[r] - dsq);
+                for (int r = 0; r < 16; ++r) ds[r] = exp2_fast(fmaf(st[r], sl2, -lse2)) * (dpt[r] - dsq);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = (kk < Sk) & (!causal | (kk <= qrow + off)) & ((window <= 0) | (kk > qrow + off - window));
+                    const float e = exp2_fast(fmaf(st[r], sl2, -lse2));
+                    ds[r] = (vis ? e : 0.f) * (dpt[r] - dsq);
+                }
             }
             bf16x8 kc[2][kNT];
 #pragma unroll
