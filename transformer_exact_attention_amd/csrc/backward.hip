@@ -285,25 +285,16 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
             const bool full = (!causal || pos0 + off >= kw0 + kWaveRows - 1) &&
                               (window <= 0 || pos0 + kWaveRows - 1 + off - window < kw0);
             f32x16 p, ds;
-            if (full) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float2 ld = row_s[buf][qi];
-                    p[r] = exp2_fast(fmaf(sc[r], sl2, -ld.x));
-                    ds[r] = p[r] * (dp[r] - ld.y);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float2 ld = row_s[buf][qi];
-                    const int pos = row0 + qi;
-                    const bool vis = (!causal | (key <= pos + off)) & ((window <= 0) | (key > pos + off - window));
-                    const float e = exp2_fast(fmaf(sc[r], sl2, -ld.x));
-                    p[r] = vis ? e : 0.f;
-                    ds[r] = p[r] * (dp[r] - ld.y);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const float2 ld = row_s[buf][qi];
+                const int pos = row0 + qi;
+                // branch-free (a branch would split the scheduling region)
+                const bool vis = full | ((!causal | (key <= pos + off)) & ((window <= 0) | (key > pos + off - window)));
+                const float e = exp2_fast(fmaf(sc[r], sl2, -ld.x));
+                p[r] = vis ? e : 0.f;
+                ds[r] = p[r] * (dp[r] - ld.y);
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
