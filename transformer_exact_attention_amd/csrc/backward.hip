@@ -187,6 +187,7 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
     const int kw0 = kb * kDkBlockRows + kWaveRows * wave;    // this wavefront's keys kw0 .. kw0 + 31
     const int key = kw0 + n;                               // this lane's key column
     const float sl2 = scale * kLog2e;
+    const uint32_t wlim = window > 0 ? (uint32_t)window : 0x80000000u;   // causal only: d >= 0
 
     // K rows of the wavefront's keys as B operands (k = d, column = key) in
     // registers; the V rows of all the workgroup's keys in LDS (read as the
@@ -284,14 +285,16 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
             // every (row, key) of the block visible?
             const bool full = (!causal || pos0 + off >= kw0 + kWaveRows - 1) &&
                               (window <= 0 || pos0 + kWaveRows - 1 + off - window < kw0);
+            const int dbase = row0 + r0 + 4 * h + off - key;
             f32x16 p, ds;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qi = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
                 const float2 ld = row_s[buf][qi];
-                const int pos = row0 + qi;
-                // branch-free (a branch would split the scheduling region)
-                const bool vis = full | ((!causal | (key <= pos + off)) & ((window <= 0) | (key > pos + off - window)));
+                // branch-free (a branch here doubles the register spills):
+                // with d = row + off - key, visible iff 0 <= d < window, one
+                // unsigned compare (no window: limit 2^31, i.e. d >= 0)
+                const bool vis = full | ((uint32_t)(dbase + 8 * (r >> 2) + (r & 3)) < wlim);
                 const float e = exp2_fast(fmaf(sc[r], sl2, -ld.x));
                 p[r] = vis ? e : 0.f;
                 ds[r] = p[r] * (dp[r] - ld.y);
