@@ -179,6 +179,18 @@ def attention_rows(q, k, v, b: int, hq: int, rows, scale=None, causal=False, win
 # ----------------------------------------------------------------------------
 # decode over a KV cache
 # ----------------------------------------------------------------------------
+def decode_key_range(L: int, window=None):
+    """Keys [lo, hi) the new query of a sequence of cached length L attends.
+
+    All cached keys [0, L) [Attention variants deep-dive, §7 KV Cache]; with a
+    sliding window of W keys only the last W of them, [max(0, L - W), L)
+    (the window reading of :func:`window_visible` at the newest position).
+    """
+    if window is None:
+        return 0, L
+    return max(0, L - window), L
+
+
 def decode_contiguous(q, k_cache, v_cache, seq_lens, scale=None, heads=None, return_lse=False, window=None):
     """One new query token per sequence over a contiguous cache.
 
@@ -198,10 +210,10 @@ def decode_contiguous(q, k_cache, v_cache, seq_lens, scale=None, heads=None, ret
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     for b, hq in pairs:
         L = int(seq_lens[b])
-        lo = max(0, L - window) if window is not None else 0
+        lo, hi = decode_key_range(L, window)
         hk = kv_head_index(hq, Hq, Hkv)
-        kb = np.asarray(k_cache[b, hk, lo:L], np.float64)
-        vb = np.asarray(v_cache[b, hk, lo:L], np.float64)
+        kb = np.asarray(k_cache[b, hk, lo:hi], np.float64)
+        vb = np.asarray(v_cache[b, hk, lo:hi], np.float64)
         ob, lb, _ = attention_head(np.asarray(q[b, hq], np.float64)[None, :], kb, vb, scale)
         o[b, hq], lse[b, hq] = ob[0], lb[0]
     return (o, lse) if return_lse else o
@@ -242,8 +254,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, block_s
                 np.asarray(paged_logical_rows(k_pages, block_table[b], hk, L, block_size), np.float64),
                 np.asarray(paged_logical_rows(v_pages, block_table[b], hk, L, block_size), np.float64))
         kb, vb = cache[(b, hk)]
-        lo = max(0, L - window) if window is not None else 0
-        ob, lb, _ = attention_head(np.asarray(q[b, hq], np.float64)[None, :], kb[lo:], vb[lo:], scale)
+        lo, hi = decode_key_range(L, window)
+        ob, lb, _ = attention_head(np.asarray(q[b, hq], np.float64)[None, :], kb[lo:hi], vb[lo:hi], scale)
         o[b, hq], lse[b, hq] = ob[0], lb[0]
     return (o, lse) if return_lse else o
 
@@ -263,20 +275,52 @@ def kv_cache_bytes(seq_len: int, num_kv_heads: int, d_head: int, batch: int = 1,
 
 
 # ----------------------------------------------------------------------------
-# the algorithm the pages give (used only to pin their equivalence claim)
+# the tiled algorithm (used only to pin the pages' equivalence claim)
 # ----------------------------------------------------------------------------
-def flash_forward_replay(q, k, v, scale, block_q: int, block_k: int, causal=False):
-    """fp64 replay of the tiled forward loop with online softmax, one head.
+def softmax_state(q_rows, k_blk, v_blk, scale, visible):
+    """Softmax summary of one block of keys for a set of query rows.
 
-    Follows [Attention variants deep-dive, §6.2 forward pseudocode]: an outer
-    loop over query blocks, an inner loop over key/value blocks; per block the
-    block max and sum of exp(S - block_max) are merged into running max/sum,
-    the accumulator is rescaled by exp(old_max - new_max) and gains
-    exp(block_max - new_max) * (P~ V); the final division by the running sum.
-    The pages leave the block probabilities undefined; they are read as the
-    unnormalised P~ = exp(S - block_max), the only reading under which the
-    final division gives softmax.  Key blocks with no visible key for a row
-    contribute nothing to that row.
+    Returns (m, l, acc): per row the largest visible score m, the sum
+    l = sum_j exp(s_j - m) and the unnormalised sum acc = sum_j exp(s_j - m) v_j
+    over the block's visible keys.  A row that sees no key of the block gets
+    the empty summary (-inf, 0, 0).  The pages' block probabilities are read
+    as these unnormalised exp(s - m) [Attention variants deep-dive, §6.2].
+    """
+    s = np.where(visible, (q_rows @ k_blk.T) * scale, NEG_INF)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(visible, np.exp(s - m_safe[:, None]), 0.0)
+    return m, e.sum(axis=1), e @ v_blk
+
+
+def merge_softmax_states(x, y):
+    """Combine the summaries of two disjoint key sets into the summary of their union.
+
+    Both are re-expressed against the larger maximum M: each summary's l and
+    acc are multiplied by exp(m - M), then added.  This is the rescaling step
+    of the online softmax [Attention variants deep-dive, §6.2 (running max and
+    sum corrected by exp of the max difference); Different attention
+    mechanisms, §4 (online softmax)]; the merge is associative and the empty
+    summary is its identity.
+    """
+    (mx, lx, ax), (my, ly, ay) = x, y
+    M = np.maximum(mx, my)
+    M_safe = np.where(np.isfinite(M), M, 0.0)
+    wx = np.where(np.isfinite(mx), np.exp(mx - M_safe), 0.0)
+    wy = np.where(np.isfinite(my), np.exp(my - M_safe), 0.0)
+    return M, wx * lx + wy * ly, wx[:, None] * ax + wy[:, None] * ay
+
+
+def tiled_forward(q, k, v, scale, block_q: int, block_k: int, causal=False, window=None):
+    """One head of attention computed tile by tile, in float64.
+
+    Query rows are taken block_q at a time; for each query block the key/value
+    blocks of block_k keys are summarised with :func:`softmax_state` and folded
+    left to right into a running summary with :func:`merge_softmax_states`;
+    the output is acc / l.  No score matrix wider than one key block exists at
+    any time, which is what the pages' tiling achieves [Attention variants
+    deep-dive, §6.2; Different attention mechanisms, §4]; the pages state the
+    result is exactly the one-shot softmax.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -285,28 +329,18 @@ def flash_forward_replay(q, k, v, scale, block_q: int, block_k: int, causal=Fals
     o = np.zeros((Sq, v.shape[1]))
     for i0 in range(0, Sq, block_q):
         rows = np.arange(i0, min(Sq, i0 + block_q))
-        qi = q[rows]
-        acc = np.zeros((len(rows), v.shape[1]))
-        row_sum = np.zeros(len(rows))
-        row_max = np.full(len(rows), NEG_INF)
+        run = (np.full(len(rows), NEG_INF), np.zeros(len(rows)), np.zeros((len(rows), v.shape[1])))
         for j0 in range(0, Sk, block_k):
             cols = np.arange(j0, min(Sk, j0 + block_k))
-            s = (qi @ k[cols].T) * scale
-            if causal:
-                s = np.where(causal_visible(rows, Sq, Sk)[:, cols], s, NEG_INF)
-            block_max = s.max(axis=1)
-            live = np.isfinite(block_max)
-            bm = np.where(live, block_max, 0.0)
-            p = np.where(live[:, None], np.exp(s - bm[:, None]), 0.0)
-            block_sum = p.sum(axis=1)
-            new_max = np.maximum(row_max, block_max)
-            nm = np.where(np.isfinite(new_max), new_max, 0.0)
-            a_old = np.where(np.isfinite(row_max), np.exp(row_max - nm), 0.0)
-            a_new = np.where(live, np.exp(bm - nm), 0.0)
-            acc = acc * a_old[:, None] + a_new[:, None] * (p @ v[cols])
-            row_sum = row_sum * a_old + block_sum * a_new
-            row_max = new_max
-        o[rows] = acc / row_sum[:, None]
+            if window is not None:
+                vis = window_visible(rows, Sq, Sk, window)[:, cols]
+            elif causal:
+                vis = causal_visible(rows, Sq, Sk)[:, cols]
+            else:
+                vis = np.ones((len(rows), len(cols)), dtype=bool)
+            run = merge_softmax_states(run, softmax_state(q[rows], k[cols], v[cols], scale, vis))
+        _, l, acc = run
+        o[rows] = acc / np.where(l > 0, l, 1.0)[:, None]
     return o
 
 

@@ -25,28 +25,36 @@ def rnd(rng, *shape):
 # ----------------------------------------------------------------------------
 # brute force: scalar Python loops over the definition (tiny inputs only)
 # ----------------------------------------------------------------------------
-def brute_force(q, k, v, Hkv, scale, causal):
-    """softmax(q.k * scale) v with explicit loops, math.exp and math.fsum.
+def brute_force_row(q, k, v, b, h, i, Hkv, scale, causal, window=None):
+    """One output row by explicit loops, math.exp and math.fsum.
 
     Query head h of a layer with Hq heads and Hkv K/V heads reads K/V head
-    h // (Hq // Hkv).
+    h // (Hq // Hkv).  Query i (of Sq, the last Sq of Sk positions) sees key j
+    when j <= i + Sk - Sq under a causal mask, and also j > i + Sk - Sq - W
+    under a window of W keys.
     """
-    B, Hq, Sq, d = q.shape
+    Hq, Sq, d = q.shape[1], q.shape[2], q.shape[3]
     Sk = k.shape[2]
-    g = Hq // Hkv
+    kh = h // (Hq // Hkv)
+    last = i + Sk - Sq
+    js = [j for j in range(Sk)
+          if (window is None or last - window < j <= last) and (window is not None or not causal or j <= last)]
+    sc = [scale * math.fsum(float(q[b, h, i, t]) * float(k[b, kh, j, t]) for t in range(d)) for j in js]
+    mx = max(sc)
+    ex = [math.exp(s - mx) for s in sc]
+    den = math.fsum(ex)
+    return np.array([math.fsum(e * float(v[b, kh, j, c]) for e, j in zip(ex, js)) / den
+                     for c in range(v.shape[3])])
+
+
+def brute_force(q, k, v, Hkv, scale, causal, window=None):
+    """softmax(q.k * scale) v for every (b, h, i), row by row (brute_force_row)."""
+    B, Hq, Sq, _ = q.shape
     out = np.zeros((B, Hq, Sq, v.shape[3]))
     for b in range(B):
         for h in range(Hq):
-            kh = h // g
             for i in range(Sq):
-                js = [j for j in range(Sk) if (not causal) or j <= i + Sk - Sq]
-                sc = [scale * math.fsum(float(q[b, h, i, t]) * float(k[b, kh, j, t]) for t in range(d))
-                      for j in js]
-                mx = max(sc)
-                ex = [math.exp(s - mx) for s in sc]
-                den = math.fsum(ex)
-                for c in range(v.shape[3]):
-                    out[b, h, i, c] = math.fsum(e * float(v[b, kh, j, c]) for e, j in zip(ex, js)) / den
+                out[b, h, i] = brute_force_row(q, k, v, b, h, i, Hkv, scale, causal, window)
     return out
 
 
@@ -270,8 +278,63 @@ def test_matches_torch_sdpa_float64(Hq, Hkv, causal):
 
 
 # ----------------------------------------------------------------------------
+# selected rows (the reference of the sampled full-size checks)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("Sq,Sk,causal,window", [(9, 9, False, None), (7, 12, True, None), (12, 12, True, None),
+                                                 (6, 11, False, 3), (10, 10, False, 4), (5, 9, True, 1)])
+def test_selected_rows_match_brute_force(Sq, Sk, causal, window):
+    # unsorted, repeated and non-contiguous rows of a GQA head (h = 5 reads K/V head 2):
+    # every row must be masked by its own index, not by its place in the selection
+    rng = np.random.default_rng(20)
+    Hq, Hkv, d = 6, 3, 4
+    q, k, v = rnd(rng, 2, Hq, Sq, d), rnd(rng, 2, Hkv, Sk, d), rnd(rng, 2, Hkv, Sk, d)
+    rows = np.array([Sq - 1, 0, 3, Sq - 1, 1][:max(1, min(5, Sq))]) % Sq
+    o, lse = A.attention_rows(q, k, v, 1, 5, rows, scale=0.8, causal=causal, window=window)
+    assert o.shape == (len(rows), d) and lse.shape == (len(rows),)
+    for r, i in enumerate(rows):
+        ref = brute_force_row(q, k, v, 1, 5, int(i), Hkv, 0.8, causal, window)
+        assert np.allclose(o[r], ref, atol=1e-13, rtol=0), (i, o[r], ref)
+
+
+def test_selected_rows_equal_the_full_head():
+    rng = np.random.default_rng(21)
+    Hq, Hkv, Sq, Sk, d = 8, 2, 40, 53, 6
+    q, k, v = rnd(rng, 2, Hq, Sq, d), rnd(rng, 2, Hkv, Sk, d), rnd(rng, 2, Hkv, Sk, d)
+    rows = np.array([39, 0, 17, 16, 33, 2])
+    for causal, window in ((False, None), (True, None), (True, 7)):
+        full, full_lse = oracle.attention(q, k, v, causal=causal, window=window, return_lse=True)
+        for b, hq in ((0, 0), (1, 3), (1, 7)):
+            o, lse = A.attention_rows(q, k, v, b, hq, rows, causal=causal, window=window)
+            assert np.allclose(o, full[b, hq, rows], atol=1e-13, rtol=0)
+            assert np.allclose(lse, full_lse[b, hq, rows], atol=1e-13, rtol=0)
+
+
+# ----------------------------------------------------------------------------
 # the pages' algorithm reaches the definition exactly
 # ----------------------------------------------------------------------------
+def test_merge_of_block_summaries_is_the_summary_of_the_union():
+    # the merged (m, l, acc) of two key sets equals the directly computed summary of their
+    # union: m the max score, l = sum exp(s - m), acc = sum exp(s - m) v
+    rng = np.random.default_rng(22)
+    q, k, v = rnd(rng, 3, 5) * 2, rnd(rng, 9, 5), rnd(rng, 9, 5)
+    vis = np.ones((3, 9), dtype=bool)
+    vis[1, :4] = False                      # row 1 sees nothing of the first set
+    a = A.softmax_state(q, k[:4], v[:4], 0.6, vis[:, :4])
+    b = A.softmax_state(q, k[4:], v[4:], 0.6, vis[:, 4:])
+    m, l, acc = A.merge_softmax_states(a, b)
+    s = np.where(vis, 0.6 * q @ k.T, -np.inf)
+    m_ref = s.max(axis=1)
+    e = np.exp(s - m_ref[:, None])
+    assert np.allclose(m, m_ref, atol=1e-13, rtol=0)
+    assert np.allclose(l, e.sum(axis=1), atol=1e-13, rtol=0)
+    assert np.allclose(acc, e @ v, atol=1e-13, rtol=0)
+    assert not np.isfinite(a[0][1]) and a[1][1] == 0 and np.all(a[2][1] == 0)   # empty summary
+    # the empty summary is the identity, on either side
+    empty = (np.full(3, -np.inf), np.zeros(3), np.zeros((3, 5)))
+    for x in (A.merge_softmax_states(empty, b), A.merge_softmax_states(b, empty)):
+        assert all(np.array_equal(p, r) for p, r in zip(x, b))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("bq,bk", [(1, 1), (3, 3), (16, 16), (64, 64), (5, 7), (64, 29)])
 def test_tiled_online_softmax_equals_one_shot(causal, bq, bk):
@@ -279,16 +342,20 @@ def test_tiled_online_softmax_equals_one_shot(causal, bq, bk):
     Sq, Sk, d = 29, 29, 8
     q, k, v = rnd(rng, Sq, d) * 2, rnd(rng, Sk, d), rnd(rng, Sk, d)
     ref, _, _ = A.attention_head(q, k, v, 0.5, causal)
-    got = A.flash_forward_replay(q, k, v, 0.5, bq, bk, causal)
+    got = A.tiled_forward(q, k, v, 0.5, bq, bk, causal)
     assert np.abs(got - ref).max() <= 1e-12
 
 
-def test_tiled_online_softmax_rectangular_causal():
+def test_tiled_online_softmax_rectangular_causal_and_window():
     rng = np.random.default_rng(14)
-    q, k, v = rnd(rng, 10, 4), rnd(rng, 23, 4), rnd(rng, 23, 4)
+    q, k, v = rnd(rng, 10, 4) * 3, rnd(rng, 23, 4), rnd(rng, 23, 4)
     ref, _, _ = A.attention_head(q, k, v, 1.1, True)
     for bq, bk in [(1, 23), (4, 6), (10, 1)]:
-        assert np.abs(A.flash_forward_replay(q, k, v, 1.1, bq, bk, True) - ref).max() <= 1e-12
+        assert np.abs(A.tiled_forward(q, k, v, 1.1, bq, bk, True) - ref).max() <= 1e-12
+    for W in (1, 5, 30):
+        ref_w, _, _ = A.attention_head(q, k, v, 1.1, window=W)
+        for bq, bk in [(3, 4), (10, 23), (1, 2)]:
+            assert np.abs(A.tiled_forward(q, k, v, 1.1, bq, bk, window=W) - ref_w).max() <= 1e-12
 
 
 @pytest.mark.parametrize("split", [1, 3, 16, 64, 100])

@@ -114,12 +114,12 @@ def test_sampled_backward_agrees_with_the_full_one(causal, window):
     k = rng.standard_normal((B, Hkv, Sk, d))
     v = rng.standard_normal((B, Hkv, Sk, d))
     do = rng.standard_normal((B, Hq, Sq, d))
-    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=causal, window=window)
+    dq, dk, dv = BW.attention_backward(q, k, v, do, causal=causal, window=window)
     rows, keys = np.array([0, 4, 8]), np.array([1, 6, 12])
     for b in range(B):
         for hk in range(Hkv):
-            sq, sk, sv = oracle.attention_backward_sampled(q, k, v, do, b, hk, rows, keys, causal=causal,
-                                                           window=window)
+            sq, sk, sv = BW.attention_backward_sampled(q, k, v, do, b, hk, rows, keys, causal=causal,
+                                                       window=window)
             assert sorted(sq) == [h for h in range(Hq) if h // 3 == hk]
             for h, got in sq.items():
                 np.testing.assert_allclose(got, dq[b, h, rows], atol=1e-12)
