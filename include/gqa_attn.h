@@ -18,9 +18,12 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; tensors are
  *    dense, row-major, with the layouts stated per call.  The library never
- *    allocates or frees device memory and keeps no mutable global state
- *    (the only memory it allocates is a KV pool's host-side bookkeeping,
- *    behind the pool's handle: gqa_kv_cache.h); calls are reentrant.
+ *    allocates or frees device memory (the only memory it allocates is a KV
+ *    pool's host-side bookkeeping, behind the pool's handle: gqa_kv_cache.h);
+ *    its only global state is the static device scratch of
+ *    attn_decode_fwd_noalloc (one array per GPU, loaded with the library's
+ *    code) and that array's per-device address.  Calls are reentrant, except
+ *    that attn_decode_fwd_noalloc calls overlapping on one GPU race.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    on it and the call returns before the kernels finish (except
  *    attn_decode_validate, which synchronises).
@@ -188,6 +191,30 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
                     int block_size, int max_blocks_per_seq,
                     float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): attn_decode_fwd with the same arguments, checks and results
+ * (the same kernels, bit for bit), minus the workspace.  Its partial results
+ * live in a static device array of GQA_DECODE_NOALLOC_MAX_BYTES bytes, one
+ * per GPU the library runs on, held until the process ends; its address is
+ * taken once per device at the first call on that device.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Sizes with attn_decode_workspace_bytes(B, Hq, d, max_seq_len) >
+ * GQA_DECODE_NOALLOC_MAX_BYTES return GQA_ERR_WORKSPACE and enqueue
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (different streams, threads or processes sharing the library
+ * instance) race on it and must be ordered by the caller.  The array needs no
+ * initial contents (every partial a call reads is written by that call).
+ */
+#define GQA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+int attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            const int32_t* seq_lens, const int32_t* block_table,
+                            int B, int Hq, int Hkv, int d, int max_seq_len,
+                            int block_size, int max_blocks_per_seq,
+                            float scale, int dtype, void* stream);
 
 /*
  * Sliding-window decode: attn_decode_fwd where query b attends only its

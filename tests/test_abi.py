@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
                             "gqa_kv_reserve", "gqa_kv_block_table", "attn_kv_append", "attn_kv_copy_blocks",
                             "attn_decode_fp8_fwd", "attn_kv_append_fp8", "attn_kv_copy_blocks_fp8",
                             "attn_prefill_window_fwd", "attn_decode_window_fwd", "attn_prefill_lse_fwd",
-                            "attn_prefill_bwd_workspace_bytes", "attn_prefill_bwd"])
+                            "attn_prefill_bwd_workspace_bytes", "attn_prefill_bwd", "attn_decode_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -205,3 +205,35 @@ def test_prefill_bwd_workspace_formula(lib):
     assert lib.attn_prefill_bwd_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 4
     assert lib.attn_prefill_bwd_workspace_bytes(1, 1, 65) == 512
     assert lib.attn_prefill_bwd_workspace_bytes(0, 4, 16) == 0
+
+
+def decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, table=None, B=2, Hq=8, Hkv=2, d=128, max_seq_len=64,
+             block_size=0, max_blocks=0, scale=0.1, dtype=1)
+    a.update(kw)
+    return lib.attn_decode_fwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lens"], a["table"], a["B"], a["Hq"],
+                                       a["Hkv"], a["d"], a["max_seq_len"], a["block_size"], a["max_blocks"],
+                                       a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lens=None), 1), (dict(B=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(scale=float("nan")), 1), (dict(table=FAKE, block_size=8, max_blocks=8), 1),
+    (dict(table=FAKE, block_size=16, max_blocks=3), 1),
+    (dict(dtype=0), 2), (dict(Hq=128, Hkv=2), 2), (dict(B=4097), 2),
+    # the workspace these sizes need exceeds the static scratch (64 MiB)
+    (dict(B=64, Hq=32, Hkv=8, max_seq_len=65536), 3),
+    (dict(B=4096, Hq=32, Hkv=8, max_seq_len=1024), 3),
+])
+def test_decode_noalloc_rejects_on_host(lib, kw, status):
+    assert decode_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_limit_matches_the_header(lib):
+    from transformer_exact_attention_amd import gqa_attn
+    text = open(HEADER).read()
+    assert "#define GQA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)" in text
+    assert gqa_attn.DECODE_NOALLOC_MAX_BYTES == 64 << 20
+    # the benchmark's decode workloads fit
+    assert lib.attn_decode_workspace_bytes(16, 32, 128, 32768) <= gqa_attn.DECODE_NOALLOC_MAX_BYTES
+    assert lib.attn_decode_workspace_bytes(64, 32, 128, 4096) <= gqa_attn.DECODE_NOALLOC_MAX_BYTES

@@ -39,6 +39,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace gqa {
 
 namespace {
@@ -594,9 +596,45 @@ hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream) {
     return launch_rows<Fmt>(a, ContiguousRows{kc, vc, a.k_scale, a.v_scale, a.Hkv, a.max_seq_len}, stream);
 }
 
+// Workspace of the allocation-free entry point: one static array per GPU.
+// Host code never passes this name to a kernel or a copy (on the host it is
+// only a stand-in for the device symbol); it uses the device address that
+// hipGetSymbolAddress returns, taken once per device with that device
+// current and kept in scratch_addr.  Every call on a GPU shares its array,
+// so calls that overlap on one GPU (two streams, two threads) race on it.
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_fmt<Bf16Kv>(a, stream); }
+
+hipError_t launch_decode_bf16_static(const DecodeArgs& a, hipStream_t stream) {
+    DecodeArgs s = a;
+    const hipError_t e = static_scratch(&s.workspace);
+    if (e != hipSuccess) return e;
+    return launch_fmt<Bf16Kv>(s, stream);
+}
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) { return launch_fmt<Fp8Kv>(a, stream); }
 

@@ -1,7 +1,8 @@
 // C ABI of libgqa_attn: host-side validation, planning and kernel launch.
 //
 // Every check runs on the host before the first HIP call, so a rejected call
-// enqueues nothing.  These calls allocate nothing and keep no state.
+// enqueues nothing.  These calls allocate nothing; the only state is the
+// per-device address of the allocation-free decode's static scratch.
 #include "../../include/gqa_attn.h"
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,8 @@
 namespace {
 
 constexpr int64_t kMaxPlane = (int64_t)1 << 31;   // elements per (b, head) plane
+static_assert(GQA_DECODE_NOALLOC_MAX_BYTES == gqa::kDecodeStaticScratchBytes,
+              "the header's limit is the size of the static scratch");
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -51,10 +54,10 @@ int prefill_check(const void* q, const void* k, const void* v, void* o, int B, i
     return GQA_OK;
 }
 
-int decode_check(const void* q, const void* kc, const void* vc, void* o, const int32_t* seq_lens,
-                 const int32_t* block_table, int B, int Hq, int Hkv, int d, int max_seq_len,
-                 int block_size, int max_blocks_per_seq, float scale, int dtype, const void* workspace,
-                 size_t workspace_bytes) {
+// Everything but the workspace.
+int decode_check_args(const void* q, const void* kc, const void* vc, void* o, const int32_t* seq_lens,
+                      const int32_t* block_table, int B, int Hq, int Hkv, int d, int max_seq_len,
+                      int block_size, int max_blocks_per_seq, float scale, int dtype) {
     if (!q || !kc || !vc || !o || !seq_lens) return GQA_ERR_INVALID_ARG;
     int st = check_heads(B, Hq, Hkv, d);
     if (st != GQA_OK) return st;
@@ -70,6 +73,16 @@ int decode_check(const void* q, const void* kc, const void* vc, void* o, const i
     const int g = Hq / Hkv;
     if (!pow2(g) || g > 32) return GQA_ERR_UNSUPPORTED;
     if (B > gqa::kDecodeMaxBatch || Hq > 65535) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+int decode_check(const void* q, const void* kc, const void* vc, void* o, const int32_t* seq_lens,
+                 const int32_t* block_table, int B, int Hq, int Hkv, int d, int max_seq_len,
+                 int block_size, int max_blocks_per_seq, float scale, int dtype, const void* workspace,
+                 size_t workspace_bytes) {
+    const int st = decode_check_args(q, kc, vc, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len, block_size,
+                                     max_blocks_per_seq, scale, dtype);
+    if (st != GQA_OK) return st;
     if (!workspace) return GQA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GQA_ERR_WORKSPACE;
     if (workspace_bytes < gqa::decode_workspace_bytes(B, Hq, d, max_seq_len)) return GQA_ERR_WORKSPACE;
@@ -87,7 +100,9 @@ const char* gqa_attn_status_string(int status) {
         case GQA_OK: return "ok";
         case GQA_ERR_INVALID_ARG: return "invalid argument";
         case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
-        case GQA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+        case GQA_ERR_WORKSPACE:
+            return "workspace missing, misaligned or too small (attn_decode_fwd_noalloc: the sizes need more "
+                   "than its static scratch of GQA_DECODE_NOALLOC_MAX_BYTES)";
         case GQA_ERR_HIP: return "HIP runtime error";
         case GQA_ERR_OUT_OF_BLOCKS: return "KV pool exhausted (free blocks or sequence ids)";
         default: return "unknown status";
@@ -166,6 +181,21 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
     gqa::DecodeArgs a{q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
                       block_table ? max_blocks_per_seq : 0, scale, workspace};
     const hipError_t e = gqa::launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            const int32_t* seq_lens, const int32_t* block_table, int B, int Hq, int Hkv, int d,
+                            int max_seq_len, int block_size, int max_blocks_per_seq, float scale, int dtype,
+                            void* stream) {
+    const int st = decode_check_args(q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
+                                     block_size, max_blocks_per_seq, scale, dtype);
+    if (st != GQA_OK) return st;
+    if (gqa::decode_workspace_bytes(B, Hq, d, max_seq_len) > GQA_DECODE_NOALLOC_MAX_BYTES)
+        return GQA_ERR_WORKSPACE;
+    gqa::DecodeArgs a{q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
+                      block_table ? max_blocks_per_seq : 0, scale, nullptr};
+    const hipError_t e = gqa::launch_decode_bf16_static(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 

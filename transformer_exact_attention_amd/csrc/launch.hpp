@@ -88,6 +88,10 @@ inline size_t decode_workspace_bytes(int B, int Hq, int d, int max_seq_len) {
     return decode_workspace_layout(B, Hq, d, max_seq_len).total;
 }
 
+// Size of the static device array behind the allocation-free decode entry
+// point (one copy per GPU, held until the process ends).
+constexpr size_t kDecodeStaticScratchBytes = (size_t)64 << 20;
+
 // Paged KV cache: new tokens [n_tokens, Hkv, d] to their slots, and whole
 // block copies; rows are row_bytes = d * element size bytes (16 | row_bytes).
 // fp8 caches add per-row fp32 scales [num_blocks, Hkv, 16] (k_scale,
@@ -116,6 +120,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
+// attn_decode_fwd with the workspace in the library's static device scratch
+// (a.workspace is ignored); the caller has checked that the sizes fit.
+hipError_t launch_decode_bf16_static(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_copy_blocks(const KvCopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_fp8(const KvAppendArgs& a, hipStream_t stream);

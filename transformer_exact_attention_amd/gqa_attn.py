@@ -29,7 +29,10 @@ EXPORTS = ("gqa_attn_abi_version", "gqa_attn_status_string", "attn_prefill_fwd",
            "gqa_kv_seq_fork", "gqa_kv_seq_release", "gqa_kv_seq_len", "gqa_kv_reserve", "gqa_kv_block_table",
            "attn_kv_append", "attn_kv_copy_blocks", "attn_decode_fp8_fwd", "attn_kv_append_fp8",
            "attn_kv_copy_blocks_fp8", "attn_prefill_window_fwd", "attn_decode_window_fwd",
-           "attn_prefill_lse_fwd", "attn_prefill_bwd_workspace_bytes", "attn_prefill_bwd")
+           "attn_prefill_lse_fwd", "attn_prefill_bwd_workspace_bytes", "attn_prefill_bwd",
+           "attn_decode_fwd_noalloc")
+
+DECODE_NOALLOC_MAX_BYTES = 64 << 20      # GQA_DECODE_NOALLOC_MAX_BYTES
 
 _lib = None
 
@@ -62,6 +65,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_workspace_bytes.argtypes = [c_int] * 4
     lib.attn_decode_fwd.restype = c_int
     lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, vp, c_size, vp]
+    lib.attn_decode_fwd_noalloc.restype = c_int
+    lib.attn_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, vp]
     lib.attn_decode_validate.restype = c_int
     lib.attn_decode_validate.argtypes = [vp, vp] + [c_int] * 5 + [vp]
     ip = ctypes.POINTER(c_int)
@@ -350,6 +355,51 @@ def attn_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                              max_blocks, float(scale), code, workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _raise(st, "attn_decode_fwd")
+    return o
+
+
+def attn_decode_fwd_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                            o: torch.Tensor, *, block_table: Optional[torch.Tensor] = None,
+                            max_seq_len: Optional[int] = None, scale: Optional[float] = None,
+                            stream=None) -> torch.Tensor:
+    """attn_decode_fwd without a workspace: the library keeps the partial results
+    in its static device scratch (nothing is allocated, here or in the library).
+
+    The caller passes the output ``o``.  Sizes whose workspace would exceed
+    DECODE_NOALLOC_MAX_BYTES raise GqaAttnError.  Calls that overlap on one GPU
+    share the scratch and race.
+    """
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q must be [B,Hq,d]; k_cache and v_cache 4-D and equal in shape")
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[3] != d or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("head dim mismatch, or o not of q's shape")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    tensors = [q, k_cache, v_cache, seq_lens, o]
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        max_blocks, block_size = block_table.shape[1], PAGE_BLOCK_SIZE
+        max_seq_len = max_blocks * PAGE_BLOCK_SIZE if max_seq_len is None else max_seq_len
+        tensors.append(block_table)
+        bt_ptr = block_table.data_ptr()
+    else:
+        max_blocks, block_size = 0, 0
+        max_seq_len = k_cache.shape[2] if max_seq_len is None else max_seq_len
+        if max_seq_len != k_cache.shape[2] or k_cache.shape[0] != B:
+            raise ValueError("contiguous cache must be [B,Hkv,S_max,d] with max_seq_len == S_max")
+        bt_ptr = None
+    _dev(*tensors)
+    code = _dtype_code(q, k_cache, v_cache, o)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_decode_fwd_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                                     seq_lens.data_ptr(), bt_ptr, B, Hq, Hkv, d, int(max_seq_len), block_size,
+                                     max_blocks, float(scale), code, _stream(stream))
+    _raise(st, "attn_decode_fwd_noalloc")
     return o
 
 
