@@ -2,18 +2,21 @@
 
 A step is one pass of the whole path over one batch of synthetic inputs:
   1. prefill: causal GQA attention, B=2, Hq=32, Hkv=8, S=8192, d=128, bf16;
-  2. decode over a contiguous KV cache: B=64, Hq=32, Hkv=8, d=128, bf16,
+  2. prefill: causal MHA attention, B=4, H=32, S=2048, d=128, bf16;
+  3. decode over a contiguous KV cache: B=64, Hq=32, Hkv=8, d=128, bf16,
      cached lengths uniform in [512, 4096];
-  3. decode over a paged KV cache (16-token blocks, random physical placement,
-     per-sequence block table): B=16, Hq=32, Hkv=8, lengths in [8192, 32768].
+  4. decode over a paged KV cache (16-token blocks, random physical placement,
+     per-sequence block table): B=16, Hq=32, lengths in [8192, 32768], with
+     Hkv = 8 (GQA), 32 (MHA) and 1 (MQA).
 All inputs are resident in device memory before the timed region.  `value` is
-the prefill throughput in TFLOP/s (algorithmic FLOPs: 4*d*Hq*B per unmasked
-query-key pair); the decode KV bandwidth (every cached K/V byte read once)
-and tokens/s are reported beside it.  Per-kernel times come from HIP events
-recorded on the stream the kernels run on.
+the GQA prefill throughput in TFLOP/s (algorithmic FLOPs: 4*d*Hq*B per
+unmasked query-key pair); the MHA prefill rate, the decode KV bandwidth
+(every cached K/V byte read once) and tokens/s are reported beside it, each
+with its roofline fraction.  Per-call times come from HIP events recorded on
+the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --only prefill|decode|paged --steps 3 --warmup 1   (profiling runs)
+       python bench.py --only prefill|mha|decode|paged|paged32|paged1 --steps 3 --warmup 1   (profiling runs)
 """
 from __future__ import annotations
 
@@ -45,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "mha", "decode", "paged", "paged32", "paged1"], default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -435,6 +438,35 @@ def calibration_copy(mib: int) -> int:
     return n
 
 
+# The step: every workload of the hot path once, in this order.  Each decode
+# call follows at least 1.3 GB of other traffic (the 5.4 GB Hkv 32 call comes
+# right before the 168 MB Hkv 1 one), which evicts the 256 MB Infinity Cache
+# without a flush inside the step.
+PHASES = ("prefill", "mha_prefill", "decode", "paged_decode", "paged_decode_hkv32", "paged_decode_hkv1")
+ONLY = {"prefill": "prefill", "mha": "mha_prefill", "decode": "decode", "paged": "paged_decode",
+        "paged32": "paged_decode_hkv32", "paged1": "paged_decode_hkv1"}
+SRC_PREFILL = ["transformer_exact_attention_amd/csrc/prefill_bf16.hip",
+               "transformer_exact_attention_amd/csrc/common.hpp"]
+SRC_DECODE = ["transformer_exact_attention_amd/csrc/decode.hip",
+              "transformer_exact_attention_amd/csrc/common.hpp",
+              "transformer_exact_attention_amd/csrc/launch.hpp"]
+
+
+def phase_workloads():
+    from transformer_exact_attention_amd import workloads as W
+    return {"prefill": W.CFG3, "mha_prefill": W.CFG2, "decode": W.CFG4, "paged_decode": W.cfg5(8),
+            "paged_decode_hkv32": W.cfg5(32), "paged_decode_hkv1": W.cfg5(1)}
+
+
+# counter profile (profiles/<name>_pmc.txt) of each phase
+TRAFFIC_PROFILE = {"prefill": "prefill_bf16_gqa_causal_B2_Hq32_Hkv8_S8192",
+                   "mha_prefill": "prefill_bf16_mha_causal_B4_H32_S2048",
+                   "decode": "decode_gqa_contig_B64_Hq32_Hkv8",
+                   "paged_decode": "decode_paged_B16_Hq32_Hkv8",
+                   "paged_decode_hkv32": "decode_paged_B16_Hq32_Hkv32",
+                   "paged_decode_hkv1": "decode_paged_B16_Hq32_Hkv1"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -463,60 +495,56 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    do_prefill = args.only in (None, "prefill")
-    do_decode = args.only in (None, "decode")
-    do_paged = args.only in (None, "paged")
-
-    wp, wd, wpg = W.CFG3, W.CFG4, W.cfg5(8)
+    wl = phase_workloads()
+    active = [p for p in PHASES if args.only is None or ONLY[args.only] == p]
+    stream = torch.cuda.current_stream()
+    calls = {}          # phase -> callable enqueueing one call on `stream`
+    info = {}           # phase -> work figures
     t_gen = time.perf_counter()
-    if do_prefill:
-        log(f"generating {wp.name}")
-        qp_np, kp_np, vp_np = W.prefill_inputs(wp)
-        qp, kp, vp = gpu(qp_np, "bf16"), gpu(kp_np, "bf16"), gpu(vp_np, "bf16")
-        op = torch.empty_like(qp)
-    if do_decode:
-        log(f"generating {wd.name}")
-        di = W.decode_inputs(wd)
-        dq, dk, dv = gpu(di.q, "bf16"), gpu(di.k_cache, "bf16"), gpu(di.v_cache, "bf16")
-        dl = gpu(di.seq_lens, "i32")
-        do_ = torch.empty_like(dq)
-        dws = gqa_attn.decode_workspace(wd.B, wd.Hq, wd.d, di.max_seq_len, dev)
-        d_bytes = W.decode_kv_bytes(di.seq_lens, wd.Hkv, wd.d)
-        del di
-    if do_paged:
-        log(f"generating {wpg.name}")
-        pi = W.decode_inputs(wpg)
-        pq, pk, pv = gpu(pi.q, "bf16"), gpu(pi.k_cache, "bf16"), gpu(pi.v_cache, "bf16")
-        pl, pt = gpu(pi.seq_lens, "i32"), gpu(pi.block_table, "i32")
-        po = torch.empty_like(pq)
-        p_max = pi.max_seq_len
-        pws = gqa_attn.decode_workspace(wpg.B, wpg.Hq, wpg.d, p_max, dev)
-        p_bytes = W.decode_kv_bytes(pi.seq_lens, wpg.Hkv, wpg.d)
-        del pi
+    cpu_inputs = None
+    for p in active:
+        w = wl[p]
+        log(f"generating {w.name}")
+        if isinstance(w, W.PrefillWorkload):
+            qn, kn, vn = W.prefill_inputs(w)
+            q, k, v = gpu(qn, "bf16"), gpu(kn, "bf16"), gpu(vn, "bf16")
+            o = torch.empty_like(q)
+            if p == "prefill":
+                cpu_inputs = (qn, kn, vn)
+            del qn, kn, vn
+            calls[p] = (lambda q=q, k=k, v=v, o=o, w=w:
+                        gqa_attn.attn_prefill_fwd(q, k, v, o, scale=w.scale_value, causal=w.causal, stream=stream))
+            info[p] = {"flops": w.flops(), "bytes": w.io_bytes()}
+        else:
+            di = W.decode_inputs(w)
+            q, kc, vc = gpu(di.q, "bf16"), gpu(di.k_cache, "bf16"), gpu(di.v_cache, "bf16")
+            lens = gpu(di.seq_lens, "i32")
+            bt = gpu(di.block_table, "i32") if w.paged else None
+            o = torch.empty_like(q)
+            msl = di.max_seq_len
+            ws = gqa_attn.decode_workspace(w.B, w.Hq, w.d, msl, dev)
+            info[p] = {"bytes": W.decode_kv_bytes(di.seq_lens, w.Hkv, w.d), "B": w.B}
+            del di
+            calls[p] = (lambda q=q, kc=kc, vc=vc, lens=lens, o=o, bt=bt, msl=msl, ws=ws, w=w:
+                        gqa_attn.attn_decode_fwd(q, kc, vc, lens, o, block_table=bt, max_seq_len=msl,
+                                                 scale=w.scale_value, workspace=ws, stream=stream))
     torch.cuda.synchronize()
     log(f"inputs resident on the GPU ({time.perf_counter() - t_gen:.1f} s)")
 
-    stream = torch.cuda.current_stream()
-
     def step(ev=None):
-        if do_prefill:
-            if ev: ev[0].record(stream)
-            gqa_attn.attn_prefill_fwd(qp, kp, vp, op, scale=wp.scale_value, causal=True, stream=stream)
-        if do_decode:
-            if ev: ev[1].record(stream)
-            gqa_attn.attn_decode_fwd(dq, dk, dv, dl, do_, scale=wd.scale_value, workspace=dws, stream=stream)
-        if do_paged:
-            if ev: ev[2].record(stream)
-            gqa_attn.attn_decode_fwd(pq, pk, pv, pl, po, block_table=pt, max_seq_len=p_max, scale=wpg.scale_value,
-                                     workspace=pws, stream=stream)
-        if ev: ev[3].record(stream)
+        for i, p in enumerate(active):
+            if ev:
+                ev[i].record(stream)
+            calls[p]()
+        if ev:
+            ev[len(active)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(active) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -525,73 +553,62 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
-    def seg(a, b):
-        return np.array([ev[a].elapsed_time(ev[b]) for ev in events]) * 1e-3   # seconds
-
-    res = {}
-    # event pairs: prefill [0,1), decode [1,2), paged [2,3)
-    order = [n for n, on in (("prefill", do_prefill), ("decode", do_decode), ("paged", do_paged)) if on]
-    idx = {"prefill": 0, "decode": 1, "paged": 2}
-    for j, n in enumerate(order):
-        a = idx[n]
-        b = idx[order[j + 1]] if j + 1 < len(order) else 3
-        res[n] = seg(a, b)
-    ms_per_step = wall / args.steps * 1e3
-
+    res = {p: np.array([ev[i].elapsed_time(ev[i + 1]) for ev in events]) * 1e-3 for i, p in enumerate(active)}
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded iid N(0,1), bf16)"}
-    src_prefill = ["transformer_exact_attention_amd/csrc/prefill_bf16.hip",
-                   "transformer_exact_attention_amd/csrc/common.hpp"]
-    src_decode = ["transformer_exact_attention_amd/csrc/decode.hip",
-                  "transformer_exact_attention_amd/csrc/common.hpp",
-                  "transformer_exact_attention_amd/csrc/launch.hpp"]
-    if do_prefill:
-        t = float(np.mean(res["prefill"]))
-        tf = wp.flops() / t / 1e12
-        out.update({"value": round(tf, 2), "unit": "TFLOP/s"})
-        traffic = kernel_traffic("prefill_bf16_gqa_causal_B2_Hq32_Hkv8_S8192", src_prefill)
-        out["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                           "kernel": "prefill_bf16_kernel<128, false>",
-                           "algorithmic_flops_per_launch": wp.flops(),
-                           "algorithmic_bytes_per_launch": wp.io_bytes(),
-                           "avg_launch_us": round(t * 1e6, 2), "min_launch_us": round(float(np.min(res["prefill"])) * 1e6, 2)}
-    if do_decode:
-        t = float(np.mean(res["decode"]))
-        out["decode"] = {"workload": wd.name, "kv_bytes": d_bytes, "avg_call_us": round(t * 1e6, 2),
-                         "min_call_us": round(float(np.min(res["decode"])) * 1e6, 2),
-                         "kv_GBps": round(d_bytes / t / 1e9, 1), "tokens_per_s": round(wd.B / t, 1),
-                         "roofline": {"bound": "hbm", "achieved": round(d_bytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
-                                      "unit": "GB/s", "frac": round(d_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
-                                      "traffic": kernel_traffic("decode_gqa_contig_B64_Hq32_Hkv8", src_decode),
-                                      "note": "split + combine kernels, one call"}}
-    if do_paged:
-        t = float(np.mean(res["paged"]))
-        out["paged_decode"] = {"workload": wpg.name, "kv_bytes": p_bytes, "avg_call_us": round(t * 1e6, 2),
-                               "min_call_us": round(float(np.min(res["paged"])) * 1e6, 2),
-                               "kv_GBps": round(p_bytes / t / 1e9, 1), "tokens_per_s": round(wpg.B / t, 1),
-                               "roofline": {"bound": "hbm", "achieved": round(p_bytes / t / 1e9, 1),
-                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                            "frac": round(p_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
-                                            "traffic": kernel_traffic("decode_paged_B16_Hq32_Hkv8", src_decode)}}
+
+    def prefill_obj(p):
+        w, t = wl[p], float(np.mean(res[p]))
+        tf = info[p]["flops"] / t / 1e12
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": kernel_traffic(TRAFFIC_PROFILE[p], SRC_PREFILL),
+                "kernel": "prefill_bf16_kernel<128, false>", "algorithmic_flops_per_launch": info[p]["flops"],
+                "algorithmic_bytes_per_launch": info[p]["bytes"], "avg_launch_us": round(t * 1e6, 2),
+                "min_launch_us": round(float(np.min(res[p])) * 1e6, 2)}
+
+    def decode_obj(p):
+        w, t = wl[p], float(np.mean(res[p]))
+        gbs = info[p]["bytes"] / t / 1e9
+        return {"workload": w.name, "kv_bytes": info[p]["bytes"], "avg_call_us": round(t * 1e6, 2),
+                "min_call_us": round(float(np.min(res[p])) * 1e6, 2), "kv_GBps": round(gbs, 1),
+                "tokens_per_s": round(w.B / t, 1),
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "traffic": kernel_traffic(TRAFFIC_PROFILE[p], SRC_DECODE),
+                             "note": "one call = split + combine kernels; traffic counts both"}}
+
+    if "prefill" in res:
+        r = prefill_obj("prefill")
+        out.update({"value": r["achieved"], "unit": "TFLOP/s"})
+        out["roofline"] = r
+    if "mha_prefill" in res:
+        out["mha_prefill"] = {"workload": wl["mha_prefill"].name, "roofline": prefill_obj("mha_prefill")}
+    for p in PHASES[2:]:
+        if p in res:
+            out[p] = decode_obj(p)
     if "value" not in out:
-        key = "decode" if do_decode else "paged_decode"
-        out.update({"value": out[key]["kv_GBps"], "unit": "GB/s"})
-        out["roofline"] = out[key]["roofline"]
-    out["config"] = {"workload": "step = causal GQA prefill B2 Hq32 Hkv8 S8192 d128 + contiguous GQA decode "
-                                 "B64 Hq32 Hkv8 L~U[512,4096] + paged GQA decode B16 Hq32 Hkv8 L~U[8192,32768]"
-                     if args.only is None else f"only {args.only}",
-                     "prefill": {"B": 2, "Hq": 32, "Hkv": 8, "S": 8192, "d": 128, "causal": True},
-                     "decode": {"B": 64, "Hq": 32, "Hkv": 8, "d": 128, "L": [512, 4096], "cache": "contiguous"},
-                     "paged_decode": {"B": 16, "Hq": 32, "Hkv": 8, "d": 128, "L": [8192, 32768], "block": 16}}
+        p = active[0]
+        r = prefill_obj(p) if p == "mha_prefill" else out[p]["roofline"]
+        out.update({"value": r["achieved"], "unit": r["unit"]})
+        out["roofline"] = r
+    out["config"] = {
+        "workload": ("step = causal GQA prefill B2 Hq32 Hkv8 S8192 d128 + causal MHA prefill B4 H32 S2048 d128 "
+                     "+ contiguous GQA decode B64 Hq32 Hkv8 L~U[512,4096] + paged decode B16 Hq32 "
+                     "L~U[8192,32768] at Hkv 8, 32 and 1 (GQA, MHA, MQA)") if args.only is None
+        else f"only {ONLY[args.only]}",
+        "prefill": {"B": 2, "Hq": 32, "Hkv": 8, "S": 8192, "d": 128, "causal": True},
+        "mha_prefill": {"B": 4, "Hq": 32, "Hkv": 32, "S": 2048, "d": 128, "causal": True},
+        "decode": {"B": 64, "Hq": 32, "Hkv": 8, "d": 128, "L": [512, 4096], "cache": "contiguous"},
+        "paged_decode": {"B": 16, "Hq": 32, "Hkv": [8, 32, 1], "d": 128, "L": [8192, 32768], "block": 16}}
 
     if args.copy_calibration_mib:
         out["copy_calibration_bytes"] = calibration_copy(args.copy_calibration_mib)
 
-    if not args.no_cpu_baseline and do_prefill:
+    if not args.no_cpu_baseline and cpu_inputs is not None:
         log("timing the fp64 oracle on a sample (CPU baseline)")
-        out["cpu_baseline"] = cpu_baseline_prefill(wp, qp_np, kp_np, vp_np)
+        out["cpu_baseline"] = cpu_baseline_prefill(wl["prefill"], *cpu_inputs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
