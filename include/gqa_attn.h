@@ -177,8 +177,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len);
  *   workspace : device, >= attn_decode_workspace_bytes(B, Hq, d, max_seq_len)
  *               bytes, 256-byte aligned; contents on entry are ignored.
  *
- * Supported: GQA_BF16, d == 128, block_size == GQA_PAGE_BLOCK_SIZE,
- * g = Hq / Hkv in {1, 2, 4, 8, 16, 32}, B <= 4096.
+ * Supported: GQA_BF16, d in {64, 128}, block_size == GQA_PAGE_BLOCK_SIZE,
+ * g = Hq / Hkv in {1, 2, 4, 8, 16, 32}, B <= 4096.  fp32 decode returns
+ * GQA_ERR_UNSUPPORTED (the decode workloads are bf16 caches; fp32 inputs
+ * are served by attn_prefill_fwd with Sq = 1).
  * GQA_ERR_INVALID_ARG for: a NULL pointer (block_table may be NULL), any size
  * <= 0, Hq % Hkv != 0, a bad scale, paged with block_size != 16 or
  * max_blocks_per_seq * block_size < max_seq_len.  GQA_ERR_WORKSPACE for a
@@ -244,7 +246,7 @@ int attn_decode_window_fwd(const void* q, const void* k_cache, const void* v_cac
  *                      [num_blocks, Hkv, 16], device;
  *   q, o             : bf16 [B, Hq, d].
  * attn_kv_append_fp8 (gqa_kv_cache.h) writes such rows.  Supported and
- * errors as attn_decode_fwd (bf16 q/o, d == 128); additionally
+ * errors as attn_decode_fwd (bf16 q/o), but d == 128 only; additionally
  * GQA_ERR_INVALID_ARG for NULL scales and GQA_ERR_UNSUPPORTED for a
  * contiguous cache whose max_seq_len is not a multiple of 16 (scales are
  * read 16 rows at a time).  Scales of rows past a sequence's length are read

@@ -94,7 +94,7 @@ def decode(lib, **kw):
     (dict(table=FAKE, block_size=8, max_blocks=8), 1),       # pages hold 16 tokens
     (dict(table=FAKE, block_size=16, max_blocks=3), 1),      # 3 * 16 < max_seq_len
     (dict(table=FAKE, block_size=16, max_blocks=0), 1),
-    (dict(d=64), 2), (dict(dtype=0), 2), (dict(Hq=128, Hkv=2), 2),   # g = 64 not supported for decode
+    (dict(d=96), 2), (dict(d=32), 2), (dict(dtype=0), 2), (dict(Hq=128, Hkv=2), 2),   # g = 64 not supported
     (dict(B=4097), 2),
     (dict(ws=None), 3), (dict(ws=FAKE + 8), 3), (dict(ws_bytes=16), 3),
 ])

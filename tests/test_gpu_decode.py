@@ -33,17 +33,17 @@ def run_paged(ga, q, kp, vp, lens, table, max_seq_len=None):
     return o
 
 
-def small_case(seed, B, Hq, Hkv, lens, S_max, paged):
+def small_case(seed, B, Hq, Hkv, lens, S_max, paged, d=128):
     lens = np.asarray(lens, np.int32)
-    q = W.normal_bf16([seed, 0], (B, Hq, 128))
+    q = W.normal_bf16([seed, 0], (B, Hq, d))
     if paged:
         max_blocks = -(-S_max // 16)
         table, nb = W.block_placement(seed, lens, max_blocks, spare_blocks=3)
-        kp = W.normal_bf16([seed, 1], (nb, Hkv, 16, 128))
-        vp = W.normal_bf16([seed, 2], (nb, Hkv, 16, 128))
+        kp = W.normal_bf16([seed, 1], (nb, Hkv, 16, d))
+        vp = W.normal_bf16([seed, 2], (nb, Hkv, 16, d))
         return q, kp, vp, lens, table
-    kc = W.normal_bf16([seed, 1], (B, Hkv, S_max, 128))
-    vc = W.normal_bf16([seed, 2], (B, Hkv, S_max, 128))
+    kc = W.normal_bf16([seed, 1], (B, Hkv, S_max, d))
+    vc = W.normal_bf16([seed, 2], (B, Hkv, S_max, d))
     return q, kc, vc, lens, None
 
 
@@ -52,9 +52,10 @@ LENS = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 700, 1024]
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (8, 1), (32, 8), (32, 1), (32, 2), (16, 1)])
 @pytest.mark.parametrize("paged", [False, True])
-def test_decode_small(ga, Hq, Hkv, paged):
-    q, kc, vc, lens, table = small_case(30 + Hq + Hkv, len(LENS), Hq, Hkv, LENS, 1024, paged)
-    note(f"decode small Hq{Hq} Hkv{Hkv} paged={paged}")
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_small(ga, Hq, Hkv, paged, d):
+    q, kc, vc, lens, table = small_case(30 + Hq + Hkv + d, len(LENS), Hq, Hkv, LENS, 1024, paged, d)
+    note(f"decode small Hq{Hq} Hkv{Hkv} d{d} paged={paged}")
     if paged:
         o = run_paged(ga, q, kc, vc, lens, table)
         ref = oracle.decode_paged(ref_f64(q, "bf16"), ref_f64(kc, "bf16"), ref_f64(vc, "bf16"), table, lens)
@@ -106,30 +107,32 @@ def test_decode_peaked(ga):
     assert_close(to_f64(o), ref, "bf16", "decode peaked", beyond_unit=True)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 1)])
-def test_decode_rising_scores_force_rescales(ga, Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 128), (32, 1, 128), (32, 1, 64), (16, 8, 64)])
+def test_decode_rising_scores_force_rescales(ga, Hq, Hkv, d):
     # key norms grow with the token index, so the running max of every piece
     # keeps rising and the lazily rescaled accumulators are redone many times
     lens = np.array([1500, 2048, 5, 600], np.int32)
-    q = W.normal([43, 0], (4, Hq, 128), "f32")
-    kc = W.normal([43, 1], (4, Hkv, 2048, 128), "f32") * (1 + np.arange(2048, dtype=np.float32) / 100)[:, None]
+    q = W.normal([43, 0], (4, Hq, d), "f32")
+    kc = W.normal([43, 1], (4, Hkv, 2048, d), "f32") * (1 + np.arange(2048, dtype=np.float32) / 100)[:, None]
     kc[:, :, 1333] *= 3
-    vc = W.normal([43, 2], (4, Hkv, 2048, 128), "f32")
+    vc = W.normal([43, 2], (4, Hkv, 2048, d), "f32")
     q, kc, vc = (W.f32_to_bf16_bits(x) for x in (q, kc, vc))
-    note(f"decode rising scores Hq{Hq} Hkv{Hkv}")
+    note(f"decode rising scores Hq{Hq} Hkv{Hkv} d{d}")
     o = run_contig(ga, q, kc, vc, lens)
     ref = oracle.decode_contiguous(ref_f64(q, "bf16"), ref_f64(kc, "bf16"), ref_f64(vc, "bf16"), lens)
     assert_close(to_f64(o), ref, "bf16", "decode rising scores", beyond_unit=True)
 
 
-def test_paged_equals_contiguous_bitwise_and_permutation_invariant(ga):
+@pytest.mark.parametrize("Hkv,d", [(8, 128), (8, 64), (1, 128), (1, 64)])
+def test_paged_equals_contiguous_bitwise_and_permutation_invariant(ga, Hkv, d):
     import torch
-    B, Hq, Hkv = 6, 32, 8
+    B, Hq = 6, 32
     lens = np.array([1, 16, 300, 513, 1000, 2048], np.int32)
-    q, kp, vp, lens, table = small_case(42, B, Hq, Hkv, lens, 2048, True)
+    q, kp, vp, lens, table = small_case(42, B, Hq, Hkv, lens, 2048, True, d)
+    note(f"paged == contiguous Hkv{Hkv} d{d}")
     o_paged = run_paged(ga, q, kp, vp, lens, table)
     # contiguous cache with the same logical contents
-    kc = np.zeros((B, Hkv, 2048, 128), np.uint16)
+    kc = np.zeros((B, Hkv, 2048, d), np.uint16)
     vc = np.zeros_like(kc)
     for b in range(B):
         t = np.arange(lens[b])

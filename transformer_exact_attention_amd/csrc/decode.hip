@@ -45,10 +45,14 @@ namespace gqa {
 
 namespace {
 
-constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kChunk = 32;               // tokens per pipeline stage (two 16-token blocks)
+// Tokens per pipeline stage: 16-token blocks per chunk.  With g <= 16 two
+// workgroups share a CU and a chunk is two blocks; with g = 32 (one workgroup
+// per CU, one wavefront per SIMD and registers to spare) a chunk is four
+// blocks, so each wavefront keeps twice the bytes in flight.
+template <int NHB>
+constexpr int chunk_blocks() { return NHB == 1 ? 2 : 2; }
 constexpr float kRescaleSlack = 8.0f;    // base-2 units, as in the prefill kernel
 constexpr int kStreamAux = 2;            // non-temporal loads: every K/V byte is read once
 
@@ -107,17 +111,27 @@ struct PagedRows {
 // exactly a bf16, so the fp8 rows are widened to bf16 operands of the same
 // MFMAs; a key's scale multiplies its score, a value row's scale multiplies
 // its probability in the P.V product (not in the row sum).
+// A lane's K piece per d-step is 8 elements at d = 32 ds + 8 q4 (the
+// 16x16x32 contraction); its V piece is D/16 elements of each of its four
+// rows at d = (D/16) c ..
+template <int D>
 struct Bf16Kv {
     static constexpr bool kFp8 = false;
-    static constexpr int kRowBytes = kD * 2;
-    struct KBuf { u32x4 r[2][4]; };                  // [block][d-step]
-    struct VBuf { u32x4 r[2][4]; };                  // [block][row]
+    static constexpr int kD = D;
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kDSteps = D / 32;           // 16x16x32 contraction steps over d
+    static constexpr int kVDwords = D / 32;          // dwords of a lane's V piece per row
+    template <int NB> struct KBuf { u32x4 r[NB][kDSteps]; };              // [block][d-step]
+    template <int NB> struct VBuf { uint32_t r[NB][4][kVDwords]; };       // [block][row][dword]
 };
-struct Fp8Kv {
+struct Fp8Kv {                                       // d = 128 only
     static constexpr bool kFp8 = true;
-    static constexpr int kRowBytes = kD;
-    struct KBuf { u32x4 r[2][2]; f32x4 s[2]; };      // 32 codes of row c at d = 32 q4 .., scales of keys 4 q4 ..
-    struct VBuf { u32x2 r[2][4]; f32x4 s[2]; };      // 8 codes of rows 4 q4 + rr at d = 8 c .., scales
+    static constexpr int kD = 128;
+    static constexpr int kRowBytes = 128;
+    static constexpr int kDSteps = 4;
+    static constexpr int kVDwords = 4;
+    template <int NB> struct KBuf { u32x4 r[NB][2]; f32x4 s[NB]; };   // 32 codes of row c at d = 32 q4 .., scales of keys 4 q4 ..
+    template <int NB> struct VBuf { u32x2 r[NB][4]; f32x4 s[NB]; };   // 8 codes of rows 4 q4 + rr at d = 8 c .., scales
 };
 
 // Eight E4M3 codes (two dwords, element e in byte e) -> eight bf16, exactly
@@ -135,37 +149,42 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     const int32_t* __restrict__ seq_lens, float* __restrict__ opart, float* __restrict__ lsepart, long long* __restrict__ prefix_out,
     int B, int Hq, int g, int P, float scale_log2, int window) {
     __shared__ long long pre[kDecodeMaxBatch + 1];
-    __shared__ long long part[kThreads];
 
+    constexpr int kD = Fmt::kD;
+    constexpr int kDSteps = Fmt::kDSteps;
+    constexpr int kNB = chunk_blocks<NHB>();          // 16-token blocks per chunk
+    constexpr int kChunk = 16 * kNB;
+    constexpr int kPV = kD / 16;                      // P.V MFMAs per block (d = kPV * m + j)
     const int tid = threadIdx.x;
     const int Hkv = Hq / g;
 
     // Token prefix sums over sequences: pre[b] = sum of L_b' for b' < b,
     // where a sliding window (window > 0) keeps only a sequence's last
     // `window` tokens: its segment is tokens [L - min(L, window), L).
-    {
-        const int per = (B + kThreads - 1) / kThreads;
+    // The first wavefront alone: lane l sums the lengths of sequences
+    // [l*per, (l+1)*per), the 64 lane sums are scanned across the wavefront,
+    // and each lane writes the running sums of its sequences.
+    if (tid < 64) {
+        const int per = (B + 63) / 64;
         const int lo = min(B, tid * per), hi = min(B, lo + per);
         long long acc = 0;
+        for (int i = lo; i < hi; ++i) acc += window > 0 ? min(seq_lens[i], window) : seq_lens[i];
+        long long x = acc;                                      // inclusive scan of the lane sums
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(x, off, 64);
+            if (tid >= off) x += y;
+        }
+        long long run = x - acc;
         for (int i = lo; i < hi; ++i) {
-            acc += window > 0 ? min(seq_lens[i], window) : seq_lens[i];
-            pre[i + 1] = acc;
+            run += window > 0 ? min(seq_lens[i], window) : seq_lens[i];
+            pre[i + 1] = run;
         }
-        part[tid] = acc;
-        __syncthreads();
-        for (int step = 1; step < kThreads; step <<= 1) {          // inclusive scan of the thread sums
-            const long long x = tid >= step ? part[tid - step] : 0;
-            __syncthreads();
-            part[tid] += x;
-            __syncthreads();
-        }
-        const long long base = tid > 0 ? part[tid - 1] : 0;
-        for (int i = lo; i < hi; ++i) pre[i + 1] += base;
         if (tid == 0) pre[0] = 0;
-        __syncthreads();
-        if (blockIdx.x == 0)
-            for (int i = tid; i <= B; i += kThreads) prefix_out[i] = pre[i];
     }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int i = tid; i <= B; i += kThreads) prefix_out[i] = pre[i];
 
     const long long W = uniform64(pre[B] * Hkv);
     const long long NW = (long long)gridDim.x * kWaves;
@@ -178,8 +197,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     const long long start = w * Q;
     const long long end = min(start + Q, W);
 
-    typedef typename Fmt::KBuf KBuf;
-    typedef typename Fmt::VBuf VBuf;
+    typedef typename Fmt::template KBuf<kNB> KBuf;
+    typedef typename Fmt::template VBuf<kNB> VBuf;
     if (start >= end) return;
 
     // A piece: the part of one segment (b, hk) inside this wavefront's share,
@@ -223,13 +242,13 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     // of heads >= g repeat the group's first head (their results are never
     // written; every column of the MFMAs is independent), so the loads need
     // no branch.
-    auto load_q = [&](bf16x8 (&qf)[NHB][4], const Piece& p) {
+    auto load_q = [&](bf16x8 (&qf)[NHB][kDSteps], const Piece& p) {
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             const int hl = hb * 16 + c;
             const uint16_t* qp = q + ((size_t)p.b * Hq + p.hk * g + (hl < g ? hl : 0)) * kD;
 #pragma unroll
-            for (int ds = 0; ds < 4; ++ds)
+            for (int ds = 0; ds < kDSteps; ++ds)
                 qf[hb][ds] = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(qp + (Fmt::kFp8 ? 32 * q4 + 8 * ds : 32 * ds + 8 * q4)));
         }
@@ -257,9 +276,9 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     };
     // Table entries of a chunk's two blocks, fetched one chunk ahead of the
     // loads that use them.
-    auto lookup = [&](int (&ph)[2], const Src& sr) {
+    auto lookup = [&](int (&ph)[kNB], const Src& sr) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < kNB; ++blk) {
             const int t0 = sr.c0 + sr.ci * kChunk + 16 * blk;
             ph[blk] = t0 < sr.p1 ? rows.lookup(table, sr.b, t0 >> 4) : 0;
         }
@@ -269,9 +288,9 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     // beyond it (chunks past the end cost no memory traffic).  With a fixed
     // number of loads per chunk the wait counts stay exact, so the next
     // chunk streams in while the current one is computed.
-    auto load = [&](KBuf& kr, VBuf& vr, const int (&ph)[2], const Src& sr) {
+    auto load = [&](KBuf& kr, VBuf& vr, const int (&ph)[kNB], const Src& sr) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < kNB; ++blk) {
             const int t0 = sr.c0 + sr.ci * kChunk + 16 * blk;
             // (uniform; kept in scalar registers so the descriptors are too)
             const int nvalid = __builtin_amdgcn_readfirstlane(min(max(sr.p1 - t0, 0), 16));
@@ -282,13 +301,23 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                 make_rsrc(rows.vbase + row * Fmt::kRowBytes, (uint32_t)nvalid * Fmt::kRowBytes);
             if constexpr (!Fmt::kFp8) {
 #pragma unroll
-                for (int ds = 0; ds < 4; ++ds)
+                for (int ds = 0; ds < kDSteps; ++ds)
                     kr.r[blk][ds] = __builtin_amdgcn_raw_buffer_load_b128(
                         krs, (uint32_t)(c * kD + 32 * ds + 8 * q4) * 2, 0, kStreamAux);
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    vr.r[blk][rr] = __builtin_amdgcn_raw_buffer_load_b128(
-                        vrs, (uint32_t)((4 * q4 + rr) * kD + 8 * c) * 2, 0, kStreamAux);
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t off = (uint32_t)((4 * q4 + rr) * kD + (kD / 16) * c) * 2;
+                    if constexpr (kD == 128) {
+                        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStreamAux);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) vr.r[blk][rr][e] = x[e];
+                    } else {
+                        const u32x2 x = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
+                        vr.r[blk][rr][0] = x[0];
+                        vr.r[blk][rr][1] = x[1];
+                    }
+                }
             } else {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
@@ -311,36 +340,48 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
         }
     };
 
-    bf16x8 qf[NHB][4], qn[NHB][4];
+    bf16x8 qf[NHB][kDSteps], qn[NHB][kDSteps];
     float ref[NHB], lsum[NHB];
-    f32x4 oacc[NHB][8];
+    f32x4 oacc[NHB][kPV];
 
     auto process = [&](const KBuf& kr, const VBuf& vr, const Piece& cur, int ci) {
-        bf16x4 pf[NHB][2];
-        // bf16 operands of the chunk: K for each block and d-step, V rows
-        // (fp8 codes widened once, for all head blocks).
-        u32x4 kop[2][4], vrow[2][4];
+        bf16x4 pf[NHB][kNB];
+        // bf16 operands of the chunk: K for each block and d-step, V row
+        // pieces (fp8 codes widened once, for all head blocks).
+        u32x4 kop[kNB][kDSteps];
+        uint32_t vrow[kNB][4][Fmt::kVDwords];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < kNB; ++blk)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
+            for (int x = 0; x < kDSteps; ++x) {
                 if constexpr (!Fmt::kFp8) {
                     kop[blk][x] = kr.r[blk][x];
-                    vrow[blk][x] = vr.r[blk][x];
                 } else {
                     const u32x4 w = kr.r[blk][x >> 1];
                     kop[blk][x] = (x & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
-                    vrow[blk][x] = fp8x8_to_bf16x8(vr.r[blk][x][0], vr.r[blk][x][1]);
+                }
+            }
+#pragma unroll
+        for (int blk = 0; blk < kNB; ++blk)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                if constexpr (!Fmt::kFp8) {
+#pragma unroll
+                    for (int e = 0; e < Fmt::kVDwords; ++e) vrow[blk][rr][e] = vr.r[blk][rr][e];
+                } else {
+                    const u32x4 w = fp8x8_to_bf16x8(vr.r[blk][rr][0], vr.r[blk][rr][1]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vrow[blk][rr][e] = w[e];
                 }
             }
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
-            float s[2][4];
+            float s[kNB][4];
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+            for (int blk = 0; blk < kNB; ++blk) {
                 f32x4 acc = f32x4{};
 #pragma unroll
-                for (int ds = 0; ds < 4; ++ds)
+                for (int ds = 0; ds < kDSteps; ++ds)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[blk][ds]),
                                                                    qf[hb][ds], acc, 0, 0, 0);
 #pragma unroll
@@ -351,24 +392,30 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                     s[blk][r] = (key >= cur.p0 && key < cur.p1) ? sc : -INFINITY;
                 }
             }
-            float tmax = s[0][0];
+            // The reference of a head (shared by its four lanes) is raised
+            // only when its chunk maximum exceeds it by the slack.  A lane
+            // first tests its own scores; only when some lane of the
+            // wavefront is over does the wavefront form the heads' maxima
+            // across lanes (a head whose lanes are all under would not be
+            // raised either way, so the result is the same).
+            float lmax = s[0][0];
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+            for (int blk = 0; blk < kNB; ++blk)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[blk][r]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
-            const bool raise = tmax > ref[hb] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(raise)) {      // wavefront-uniform branch
+                for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, s[blk][r]);
+            if (__builtin_amdgcn_ballot_w64(lmax * scale_log2 > ref[hb] + kRescaleSlack)) {   // uniform branch
+                float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+                const bool raise = tmax > ref[hb] + kRescaleSlack;
                 const float ref_new = raise ? tmax : ref[hb];
                 const float alpha = exp2_fast(ref[hb] - ref_new);
                 ref[hb] = ref_new;
                 lsum[hb] *= alpha;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) oacc[hb][j] *= alpha;
+                for (int j = 0; j < kPV; ++j) oacc[hb][j] *= alpha;
             }
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+            for (int blk = 0; blk < kNB; ++blk) {
                 float p[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -384,11 +431,12 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                 pf[hb][blk] = __builtin_bit_cast(bf16x4, x);
             }
         }
-        // O^T += V^T . P^T; MFMA j covers d = 8*m + j.
+        // O^T += V^T . P^T; MFMA j covers d = kPV*m + j (m = 0..15, the lane
+        // group c holding d-piece m).
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < kNB; ++blk) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < kPV; ++j) {
                 const int dw = j >> 1;
                 u32x2 a;
                 if (j & 1) {
@@ -407,7 +455,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     };
 
     // Finish a piece: each lane summed its own keys; the four lanes of a head
-    // share its reference.  Lane holds head hb*16 + c, d = 32*q4 + 8*r + j.
+    // share its reference.  Lane holds head hb*16 + c, d = kPV*(4*q4 + r) + j.
     auto finish = [&](const Piece& cur) {
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
@@ -417,14 +465,15 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
             if (hl < g) {
                 const size_t row = ((size_t)cur.b * Hq + cur.hk * g + hl) * P + cur.slot;
                 const float inv = 1.f / lt;
-                float* dst = opart + row * kD + 32 * q4;
+                float* dst = opart + row * kD + 4 * kPV * q4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    f32x4 lo = {oacc[hb][0][r] * inv, oacc[hb][1][r] * inv, oacc[hb][2][r] * inv, oacc[hb][3][r] * inv};
-                    f32x4 hi = {oacc[hb][4][r] * inv, oacc[hb][5][r] * inv, oacc[hb][6][r] * inv, oacc[hb][7][r] * inv};
-                    *reinterpret_cast<f32x4*>(dst + 8 * r) = lo;
-                    *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = hi;
-                }
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j4 = 0; j4 < kPV; j4 += 4) {
+                        const f32x4 x = {oacc[hb][j4][r] * inv, oacc[hb][j4 + 1][r] * inv, oacc[hb][j4 + 2][r] * inv,
+                                         oacc[hb][j4 + 3][r] * inv};
+                        *reinterpret_cast<f32x4*>(dst + kPV * r + j4) = x;
+                    }
                 if (q4 == 0) lsepart[row] = ref[hb] + __builtin_amdgcn_logf(lt);   // v_log_f32: log2
             }
         }
@@ -434,7 +483,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     // entries.
     KBuf ka, kb;
     VBuf va, vb;
-    int pha[2], phb[2];
+    int pha[kNB], phb[kNB];
     auto pair = [&](const Piece& cur, const Piece& nxt, int ci, bool last) {
         lookup(pha, src_of(cur, nxt, ci + 2));
         load(kb, vb, phb, src_of(cur, nxt, ci + 1));
@@ -461,7 +510,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
             ref[hb] = -INFINITY;
             lsum[hb] = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) oacc[hb][j] = f32x4{};
+            for (int j = 0; j < kPV; ++j) oacc[hb][j] = f32x4{};
         }
         const int last = ((cur.nchunks + 1) & ~1) - 2;
         for (int ci = 0; ci < last; ci += 2) pair(cur, nxt, ci, false);
@@ -472,29 +521,28 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-            for (int ds = 0; ds < 4; ++ds) qf[hb][ds] = qn[hb][ds];
+            for (int ds = 0; ds < kDSteps; ++ds) qf[hb][ds] = qn[hb][ds];
     }
 }
 
-// One workgroup of kCombineWaves wavefronts per (query head, sequence); lane
-// owns d = 2*lane, 2*lane+1.  Wavefront w merges partials w, w + kCombineWaves,
-// ... in one pass with a running maximum (the rescale step of the tiled
-// online softmax), issuing the loads of several partials at once; the
-// wavefronts' results are then merged in LDS in a fixed order.  With few
-// partials per row (short caches) one wavefront per row does it all.
-constexpr int kCombineBatch = 4;         // partials in flight per wavefront
+// Combine: the partial results of a (sequence, query head) row are merged
+// with a running maximum, weights 2^(lse_s - max), the rescale step of the
+// tiled online softmax applied across pieces.  Every kernel finds a row's
+// partials from the same share arithmetic as the split kernel.
+//
+// Few partials per row (caches up to 7,936 tokens): one wavefront per row,
+// lane owning d = kE*lane .., merging the partials in order.
+constexpr int kCombineBatch = 4;         // partials in flight per lane
 constexpr int kCombineFewPartials = 32;  // at most this many per row: one wavefront
 
-template <int kCombineWaves>
-__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
+template <int kD>
+__global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ lsepart, const long long* __restrict__ prefix,
     uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW) {
-    __shared__ float red[kCombineWaves][2][64 + 1];
-    __shared__ float red_m[kCombineWaves], red_den[kCombineWaves];
+    constexpr int kE = kD / 64;          // output elements per lane: d = kE * lane ..
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x;
     const int Hkv = Hq / g;
     const long long L = prefix[b + 1] - prefix[b];
     float m = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f;
@@ -504,15 +552,18 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
         const long long S = prefix[b] * Hkv + (long long)(hq / g) * L;
         const int np = (int)((S + L - 1) / Q - S / Q) + 1;
         const size_t row0 = ((size_t)b * Hq + hq) * P;
-        for (int s0 = wave; s0 < np; s0 += kCombineWaves * kCombineBatch) {
+        for (int s0 = 0; s0 < np; s0 += kCombineBatch) {
             float x[kCombineBatch];
             float2 v[kCombineBatch];
 #pragma unroll
             for (int u = 0; u < kCombineBatch; ++u) {
-                const int s = s0 + u * kCombineWaves;
+                const int s = s0 + u;
                 const int sc = s < np ? s : np - 1;
                 x[u] = s < np ? lsepart[row0 + sc] : -INFINITY;
-                v[u] = *reinterpret_cast<const float2*>(opart + (row0 + sc) * kD + 2 * lane);
+                if constexpr (kE == 2)
+                    v[u] = *reinterpret_cast<const float2*>(opart + (row0 + sc) * kD + 2 * lane);
+                else
+                    v[u] = float2{opart[(row0 + sc) * kD + lane], 0.f};
             }
 #pragma unroll
             for (int u = 0; u < kCombineBatch; ++u) {
@@ -526,30 +577,91 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
             }
         }
     }
-    red[wave][0][lane] = a0;
-    red[wave][1][lane] = a1;
-    if (lane == 0) {
-        red_m[wave] = m;
-        red_den[wave] = den;
+    float o0 = 0.f, o1 = 0.f;
+    if (m != -INFINITY) {
+        o0 = a0 / den;
+        o1 = a1 / den;
+    }
+    if constexpr (kE == 2)
+        reinterpret_cast<uint32_t*>(o + ((size_t)b * Hq + hq) * kD)[lane] = pack_bf16x2(o0, o1);
+    else
+        o[((size_t)b * Hq + hq) * kD + lane] = (uint16_t)(pack_bf16x2(o0, 0.f) & 0xffffu);
+}
+
+// Many partials per row: a workgroup of 256 threads per row.  Thread t owns
+// the 4-float column c = t % kCols of the row and reads partials
+// t / kCols, t / kCols + kGroups, ..., up to kWideBatch of them per round,
+// all loads issued together; the kGroups running results of a column are
+// then merged in LDS in a fixed order, so the output is reproducible bit for
+// bit.
+constexpr int kWideBatch = 8;
+
+template <int kD>
+__global__ __launch_bounds__(256) void decode_combine_wide_kernel(
+    const float* __restrict__ opart, const float* __restrict__ lsepart, const long long* __restrict__ prefix,
+    uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW) {
+    constexpr int kCols = kD / 4;
+    constexpr int kGroups = 256 / kCols;
+    __shared__ f32x4 red_acc[kGroups][kCols];
+    __shared__ float red_m[kGroups], red_den[kGroups];
+    const int hq = blockIdx.x;
+    const int b = blockIdx.y;
+    const int t = threadIdx.x;
+    const int col = t % kCols, grp = t / kCols;
+    const int Hkv = Hq / g;
+    const long long L = prefix[b + 1] - prefix[b];
+    float m = -INFINITY, den = 0.f;
+    f32x4 acc = f32x4{};
+    if (L > 0) {
+        const long long W = prefix[B] * Hkv;
+        const long long Q = share_tokens(W, NW);
+        const long long S = prefix[b] * Hkv + (long long)(hq / g) * L;
+        const int np = (int)((S + L - 1) / Q - S / Q) + 1;
+        const size_t row0 = ((size_t)b * Hq + hq) * P;
+        for (int s0 = grp; s0 < np; s0 += kGroups * kWideBatch) {
+            float x[kWideBatch];
+            f32x4 v[kWideBatch];
+#pragma unroll
+            for (int u = 0; u < kWideBatch; ++u) {
+                const int s = s0 + u * kGroups;
+                const int sc = s < np ? s : np - 1;
+                x[u] = s < np ? lsepart[row0 + sc] : -INFINITY;
+                v[u] = *reinterpret_cast<const f32x4*>(opart + (row0 + sc) * kD + 4 * col);
+            }
+#pragma unroll
+            for (int u = 0; u < kWideBatch; ++u) {
+                const float mn = fmaxf(m, x[u]);
+                const float sc = mn == m ? 1.f : exp2_fast(m - mn);
+                const float wgt = x[u] == -INFINITY ? 0.f : exp2_fast(x[u] - mn);
+                den = den * sc + wgt;
+                acc = acc * sc + wgt * v[u];
+                m = mn;
+            }
+        }
+    }
+    red_acc[grp][col] = acc;
+    if (col == 0) {
+        red_m[grp] = m;
+        red_den[grp] = den;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (grp == 0) {
         float M = red_m[0];
 #pragma unroll
-        for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red_m[w]);
-        float dt = 0.f, o0 = 0.f, o1 = 0.f;
+        for (int k = 1; k < kGroups; ++k) M = fmaxf(M, red_m[k]);
+        float dt = 0.f;
+        f32x4 r = f32x4{};
         if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < kCombineWaves; ++w) {
-                const float f = red_m[w] == -INFINITY ? 0.f : exp2_fast(red_m[w] - M);
-                dt += f * red_den[w];
-                o0 += f * red[w][0][lane];
-                o1 += f * red[w][1][lane];
+            for (int k = 0; k < kGroups; ++k) {
+                const float f = red_m[k] == -INFINITY ? 0.f : exp2_fast(red_m[k] - M);
+                dt += f * red_den[k];
+                r += f * red_acc[k][col];
             }
-            o0 /= dt;
-            o1 /= dt;
+            r /= dt;
         }
-        reinterpret_cast<uint32_t*>(o + ((size_t)b * Hq + hq) * kD)[lane] = pack_bf16x2(o0, o1);
+        const u32x2 w = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+        *reinterpret_cast<u32x2*>(o + ((size_t)b * Hq + hq) * kD + 4 * col) = w;
     }
 }
 
@@ -560,6 +672,7 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return hipErrorInvalidDevice;
     const int nwg = cus * (NHB == 1 ? 2 : 1);                      // every workgroup resident at once
+    constexpr int kD = Fmt::kD;
     const DecodeWorkspace ws = decode_workspace_layout(a.B, a.Hq, kD, a.max_seq_len);
     char* base = static_cast<char*>(a.workspace);
     float* opart = reinterpret_cast<float*>(base + ws.part_o);
@@ -574,11 +687,11 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (P <= kCombineFewPartials)
-        hipLaunchKernelGGL(decode_combine_kernel<1>, dim3(a.Hq, a.B), dim3(64), 0, stream, opart, lsepart, prefix,
-                           static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
+        hipLaunchKernelGGL((decode_combine_kernel<kD>), dim3(a.Hq, a.B), dim3(64), 0, stream, opart, lsepart,
+                           prefix, static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
     else
-        hipLaunchKernelGGL(decode_combine_kernel<4>, dim3(a.Hq, a.B), dim3(256), 0, stream, opart, lsepart, prefix,
-                           static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
+        hipLaunchKernelGGL((decode_combine_wide_kernel<kD>), dim3(a.Hq, a.B), dim3(256), 0, stream, opart, lsepart,
+                           prefix, static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
     return hipGetLastError();
 }
 
@@ -627,13 +740,15 @@ hipError_t static_scratch(void** out) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_fmt<Bf16Kv>(a, stream); }
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+    return a.d == 64 ? launch_fmt<Bf16Kv<64>>(a, stream) : launch_fmt<Bf16Kv<128>>(a, stream);
+}
 
 hipError_t launch_decode_bf16_static(const DecodeArgs& a, hipStream_t stream) {
     DecodeArgs s = a;
     const hipError_t e = static_scratch(&s.workspace);
     if (e != hipSuccess) return e;
-    return launch_fmt<Bf16Kv>(s, stream);
+    return launch_decode_bf16(s, stream);
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) { return launch_fmt<Fp8Kv>(a, stream); }

@@ -69,7 +69,7 @@ int decode_check_args(const void* q, const void* kc, const void* vc, void* o, co
         if (max_blocks_per_seq <= 0) return GQA_ERR_INVALID_ARG;
         if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return GQA_ERR_INVALID_ARG;
     }
-    if (dtype != GQA_BF16 || d != 128) return GQA_ERR_UNSUPPORTED;
+    if (dtype != GQA_BF16 || (d != 64 && d != 128)) return GQA_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
     if (!pow2(g) || g > 32) return GQA_ERR_UNSUPPORTED;
     if (B > gqa::kDecodeMaxBatch || Hq > 65535) return GQA_ERR_UNSUPPORTED;
@@ -222,6 +222,7 @@ int attn_decode_fp8_fwd(const void* q, const void* k_cache, const void* v_cache,
     const int st = decode_check(q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
                                 block_size, max_blocks_per_seq, scale, GQA_BF16, workspace, workspace_bytes);
     if (st != GQA_OK) return st;
+    if (d != 128) return GQA_ERR_UNSUPPORTED;
     // a contiguous cache's scale rows are read 16 at a time from block starts
     if (!block_table && max_seq_len % GQA_PAGE_BLOCK_SIZE != 0) return GQA_ERR_UNSUPPORTED;
     gqa::DecodeArgs a{q, k_cache, v_cache, o, seq_lens, block_table, B, Hq, Hkv, d, max_seq_len,
