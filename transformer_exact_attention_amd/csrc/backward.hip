@@ -227,7 +227,12 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
 
     // Query tiles: for each head of the group, the tiles holding a row that
     // sees one of the workgroup's keys (causal: rows i >= key - off; window W:
-    // also i < key - off + W).
+    // also i < key - off + W).  They are walked tile-major over the group's
+    // heads, from the last tile down: every workgroup of a K/V head starts on
+    // the same tile at the same time (causal: the key blocks differ only in
+    // where they stop), so the Q and dO tiles are fetched once into the L2
+    // they share (the key blocks of a head run on one XCD) instead of once
+    // per workgroup.
     const int first_tile = causal ? max(0, kb * kDkBlockRows - off) / kTileRows : 0;
     int end_tile = (Sq + kTileRows - 1) / kTileRows;
     if (window > 0)
@@ -235,16 +240,17 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
     const int n_per_head = max(0, end_tile - first_tile);
     const int total = g * n_per_head;
     u32x4 qr[kRegs], dr[kRegs];
+    auto tile_row0 = [&](int it) { return (first_tile + n_per_head - 1 - it / g) * kTileRows; };
     auto fetch = [&](int it) {
-        const int hq = hk * g + it / n_per_head;
-        const int row0 = (first_tile + it % n_per_head) * kTileRows;
+        const int hq = hk * g + it % g;
+        const int row0 = tile_row0(it);
         const size_t base = ((size_t)b * Hq + hq) * Sq;
         load_rows<D, kDkThreads>(qr, q + base * D, row0, Sq);
         load_rows<D, kDkThreads>(dr, dout + base * D, row0, Sq);
     };
     auto stash = [&](int it, int buf) {
-        const int hq = hk * g + it / n_per_head;
-        const int row0 = (first_tile + it % n_per_head) * kTileRows;
+        const int hq = hk * g + it % g;
+        const int row0 = tile_row0(it);
         const size_t base = ((size_t)b * Hq + hq) * Sq;
         store_rows<D, kDkThreads>((lds_char*)q_raw[buf], qr);
         store_rows<D, kDkThreads>((lds_char*)d_raw[buf], dr);
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
     for (int it = 0; it < total; ++it) {
         const int buf = it & 1;
         if (it + 1 < total) fetch(it + 1);                 // in flight while this tile is computed
-        const int row0 = (first_tile + it % n_per_head) * kTileRows;
+        const int row0 = tile_row0(it);
         const lds_char* qt = (const lds_char*)q_raw[buf];
         const lds_char* dt = (const lds_char*)d_raw[buf];
 #pragma unroll
@@ -351,14 +357,32 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     // 1-D grid, query block slowest; causal: the last query blocks see the
-    // most keys, so they start first.  The heads of a group are adjacent
-    // (their shared K/V tiles meet in cache).
+    // most keys, so they start first.  Workgroup id L runs on XCD L % 8; when
+    // the K/V groups (b, hk) divide among the 8 XCDs, XCD x takes whole
+    // groups (all g heads, every query block), so a group's K/V tiles, which
+    // all its workgroups walk from key 0 up, are fetched into one L2; each
+    // XCD still gets an equal share of every query block.
     const int nqb = (Sq + kDqBlockRows - 1) / kDqBlockRows;
-    const int planes = (int)gridDim.x / nqb;                                      // Hq * B
-    const int rank = (int)blockIdx.x / planes;
+    const int g = Hq / Hkv;
+    const int L = (int)blockIdx.x;
+    const int ngroups = Hkv * ((int)gridDim.x / nqb / Hq);                      // Hkv * B
+    int rank, hq, b;
+    if ((ngroups & 7) == 0) {
+        const int per_rank = ngroups / 8 * g;                                   // items of one rank per XCD
+        const int j = L >> 3;
+        rank = j / per_rank;
+        const int rem = j % per_rank;
+        const int grp = (L & 7) * (ngroups / 8) + rem / g;
+        b = grp / Hkv;
+        hq = (grp % Hkv) * g + rem % g;
+    } else {
+        const int planes = (int)gridDim.x / nqb;                                // Hq * B
+        rank = L / planes;
+        hq = L % Hq;
+        b = (L % planes) / Hq;
+    }
     const int qb = causal ? nqb - 1 - rank : rank;
-    const int hq = (int)blockIdx.x % Hq, b = ((int)blockIdx.x % planes) / Hq;
-    const int g = Hq / Hkv, hk = hq / g;
+    const int hk = hq / g;
     const int off = Sk - Sq;
     const int qw0 = qb * kDqBlockRows + kWaveRows * wave;    // this wavefront's rows qw0 .. qw0 + 31
     const int qrow = qw0 + n;                              // this lane's query column
