@@ -26,11 +26,12 @@ from transformer_exact_attention_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-# |lse_gpu - lse_ref|.  The bf16 kernel sums the probabilities after rounding
-# them to bf16 (the same values it multiplies V with, so o's numerator and
-# denominator agree); each carries a relative error of at most 2^-9, which
-# does not average out on rows with few keys, so ln(l) is off by up to about
-# 2^-9.  The fp32 kernel sums unrounded probabilities.
+# |lse_gpu - lse_ref|.  The bf16 kernel sums fp32 probabilities on its common
+# path and bf16-rounded ones (the values it multiplies V with) on its
+# recomputing path, which every row takes for its first tile and for any tile
+# whose sum passes 2^8; a rounded term carries a relative error of at most
+# 2^-9, which does not average out on rows with few keys, so ln(l) is off by
+# up to about 2^-9.  The fp32 kernel sums unrounded probabilities.
 LSE_TOL = {"bf16": 2.0 ** -8, "f32": 1e-4}
 
 
