@@ -62,16 +62,16 @@ def test_window_covering_everything_equals_causal_bitwise(ga, dtype):
     assert torch.equal(a, b)
 
 
-def _decode_case(seed, B, Hq, Hkv, lens, S_max, paged):
+def _decode_case(seed, B, Hq, Hkv, lens, S_max, paged, d=128):
     lens = np.asarray(lens, np.int32)
-    q = W.normal_bf16([seed, 0], (B, Hq, 128))
+    q = W.normal_bf16([seed, 0], (B, Hq, d))
     if paged:
         table, nb = W.block_placement(seed, lens, -(-S_max // 16), spare_blocks=3)
-        kp = W.normal_bf16([seed, 1], (nb, Hkv, 16, 128))
-        vp = W.normal_bf16([seed, 2], (nb, Hkv, 16, 128))
+        kp = W.normal_bf16([seed, 1], (nb, Hkv, 16, d))
+        vp = W.normal_bf16([seed, 2], (nb, Hkv, 16, d))
         return q, kp, vp, lens, table
-    kc = W.normal_bf16([seed, 1], (B, Hkv, S_max, 128))
-    vc = W.normal_bf16([seed, 2], (B, Hkv, S_max, 128))
+    kc = W.normal_bf16([seed, 1], (B, Hkv, S_max, d))
+    vc = W.normal_bf16([seed, 2], (B, Hkv, S_max, d))
     return q, kc, vc, lens, None
 
 
@@ -89,10 +89,11 @@ LENS = [0, 1, 15, 16, 17, 63, 255, 256, 700, 1024]
 
 
 @pytest.mark.parametrize("paged", [False, True])
-@pytest.mark.parametrize("Hq,Hkv,Wn", [(32, 8, 16), (32, 8, 100), (32, 32, 1), (32, 1, 512), (16, 4, 300)])
-def test_decode_window_matches_oracle(ga, paged, Hq, Hkv, Wn):
-    note(f"window decode Hq{Hq} Hkv{Hkv} W{Wn} paged={paged}")
-    q, kc, vc, lens, table = _decode_case(50 + Wn, len(LENS), Hq, Hkv, LENS, 1024, paged)
+@pytest.mark.parametrize("Hq,Hkv,Wn,d", [(32, 8, 16, 128), (32, 8, 100, 128), (32, 32, 1, 128), (32, 1, 512, 128),
+                                         (16, 4, 300, 128), (32, 8, 100, 64), (32, 1, 17, 64)])
+def test_decode_window_matches_oracle(ga, paged, Hq, Hkv, Wn, d):
+    note(f"window decode Hq{Hq} Hkv{Hkv} W{Wn} d{d} paged={paged}")
+    q, kc, vc, lens, table = _decode_case(50 + Wn + d, len(LENS), Hq, Hkv, LENS, 1024, paged, d)
     o = run_decode(ga, q, kc, vc, lens, table, 1024, Wn)
     if paged:
         ref = oracle.decode_paged(ref_f64(q, "bf16"), ref_f64(kc, "bf16"), ref_f64(vc, "bf16"), table, lens, window=Wn)

@@ -22,29 +22,29 @@ def ga():
     return gqa_attn
 
 
-def case(seed, B, Hq, Hkv, lens, S_max, paged):
+def case(seed, B, Hq, Hkv, lens, S_max, paged, d=128):
     lens = np.asarray(lens, np.int32)
-    q = W.normal_bf16([seed, 0], (B, Hq, 128))
+    q = W.normal_bf16([seed, 0], (B, Hq, d))
     if paged:
         max_blocks = -(-S_max // 16)
         table, nb = W.block_placement(seed, lens, max_blocks, spare_blocks=2)
-        k = W.normal_bf16([seed, 1], (nb, Hkv, 16, 128))
-        v = W.normal_bf16([seed, 2], (nb, Hkv, 16, 128))
+        k = W.normal_bf16([seed, 1], (nb, Hkv, 16, d))
+        v = W.normal_bf16([seed, 2], (nb, Hkv, 16, d))
         return q, k, v, lens, table, max_blocks * 16
-    k = W.normal_bf16([seed, 1], (B, Hkv, S_max, 128))
-    v = W.normal_bf16([seed, 2], (B, Hkv, S_max, 128))
+    k = W.normal_bf16([seed, 1], (B, Hkv, S_max, d))
+    v = W.normal_bf16([seed, 2], (B, Hkv, S_max, d))
     return q, k, v, lens, None, S_max
 
 
-def run_both(ga, seed, B, Hq, Hkv, lens, S_max, paged):
+def run_both(ga, seed, B, Hq, Hkv, lens, S_max, paged, d=128):
     import torch
-    q, k, v, lens, table, msl = case(seed, B, Hq, Hkv, lens, S_max, paged)
+    q, k, v, lens, table, msl = case(seed, B, Hq, Hkv, lens, S_max, paged, d)
     qg, kg, vg, lg = to_gpu(q, "bf16"), to_gpu(k, "bf16"), to_gpu(v, "bf16"), to_gpu(lens, "i32")
     tg = to_gpu(table, "i32") if paged else None
     o_ref = torch.full_like(qg, float("nan"))
     o_new = torch.full_like(qg, float("nan"))
-    ws = ga.decode_workspace(B, Hq, 128, msl, qg.device)
-    note(f"noalloc decode B{B} Hq{Hq} Hkv{Hkv} S_max{S_max} paged={paged}")
+    ws = ga.decode_workspace(B, Hq, d, msl, qg.device)
+    note(f"noalloc decode B{B} Hq{Hq} Hkv{Hkv} S_max{S_max} d{d} paged={paged}")
     ga.attn_decode_fwd(qg, kg, vg, lg, o_ref, block_table=tg, max_seq_len=msl, workspace=ws)
     torch.cuda.synchronize()
     before = torch.cuda.memory_allocated()
@@ -65,6 +65,7 @@ def test_noalloc_decode_matches_the_workspace_call_on_consecutive_calls(ga):
     run_both(ga, 71, 4, 8, 2, [300, 5, 0, 129], 300, False)           # smaller, contiguous
     run_both(ga, 72, 16, 32, 1, big, 4096, True)                      # larger again, MQA
     run_both(ga, 73, 3, 4, 4, [1, 16, 2], 16, False)                  # smallest, MHA
+    run_both(ga, 74, 5, 16, 2, [700, 0, 33, 256, 1], 768, True, d=64)  # head dim 64
 
 
 def test_noalloc_decode_rejects_sizes_beyond_its_scratch(ga):
