@@ -315,8 +315,12 @@ __global__ __launch_bounds__(kDkThreads) void bwd_dkdv_kernel(
                 }
             }
         }
+        // The other buffer was last read while computing the previous tile,
+        // which every wavefront finished before the barrier that published
+        // this tile: it can be refilled at once.  One barrier per tile then
+        // makes the new tile visible (and keeps any wavefront from running
+        // more than one tile ahead).
         if (it + 1 < total) {
-            __syncthreads();                                // everyone is done with the other buffer
             stash(it + 1, buf ^ 1);
             __syncthreads();
         }
@@ -489,8 +493,9 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(
                 for (int t = 0; t < kNT; ++t) dqa[t] = mfma32(kc[s2][t], dsb, dqa[t]);
             }
         }
+        // (one barrier per tile, as in the dK/dV kernel: the other buffer
+        // was last read in the previous tile, before the last barrier)
         if (it + 1 < ntiles) {
-            __syncthreads();
             stash(buf ^ 1);
             __syncthreads();
         }
