@@ -47,12 +47,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-// Tokens per pipeline stage: 16-token blocks per chunk.  With g <= 16 two
-// workgroups share a CU and a chunk is two blocks; with g = 32 (one workgroup
-// per CU, one wavefront per SIMD and registers to spare) a chunk is four
-// blocks, so each wavefront keeps twice the bytes in flight.
-template <int NHB>
-constexpr int chunk_blocks() { return NHB == 1 ? 2 : 2; }
+// Tokens per pipeline stage: 16-token blocks per chunk (two chunks in flight
+// per wavefront).  Longer chunks measured no faster: four blocks at g = 32
+// (one wavefront per SIMD), three for fp8 caches.
+constexpr int kChunkBlocks = 2;
 constexpr float kRescaleSlack = 8.0f;    // base-2 units, as in the prefill kernel
 constexpr int kStreamAux = 2;            // non-temporal loads: every K/V byte is read once
 
@@ -152,7 +150,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
 
     constexpr int kD = Fmt::kD;
     constexpr int kDSteps = Fmt::kDSteps;
-    constexpr int kNB = chunk_blocks<NHB>();          // 16-token blocks per chunk
+    constexpr int kNB = kChunkBlocks;                 // 16-token blocks per chunk
     constexpr int kChunk = 16 * kNB;
     constexpr int kPV = kD / 16;                      // P.V MFMAs per block (d = kPV * m + j)
     const int tid = threadIdx.x;
