@@ -69,20 +69,22 @@ struct Tile {
 };
 
 // 64 x D bf16 rows [row0, row0 + 64) of a [rows_total, D] matrix -> LDS tile.
-// Rows past rows_total repeat the last row (finite values whose products the
-// callers multiply by a zero probability); the loads stay unconditional, so
-// no branch keeps the compiler from overlapping them with the tile's work.
-// 256 threads, 16-byte chunks.
+// The loads go through a buffer resource that starts at row0 and ends at the
+// matrix's last row (row0 is wavefront-uniform, so the resource is scalar
+// and each lane's offset is the same for every tile): rows past rows_total
+// read as zeros, finite values whose products the callers multiply by a
+// zero probability, and the loads stay unconditional, so no branch keeps
+// the compiler from overlapping them with the tile's work.
 template <int D, int NT = kBwdThreads>
 __device__ __forceinline__ void load_rows(u32x4 (&reg)[kTileRows * D / 8 / NT], const uint16_t* base,
                                           int row0, int rows_total) {
     constexpr int kChunks = D / 8;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)row0 * D, (uint32_t)(rows_total - row0) * D * 2);
 #pragma unroll
     for (int x = 0; x < kTileRows * kChunks / NT; ++x) {
         const int i = x * NT + (int)threadIdx.x;
-        const int r = i / kChunks, c = i % kChunks;
-        const int row = min(row0 + r, rows_total - 1);
-        reg[x] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + 8 * c);
+        const int rr = i / kChunks, c = i % kChunks;
+        reg[x] = buffer_load16(r, (uint32_t)((rr * D + 8 * c) * 2));
     }
 }
 template <int D, int NT = kBwdThreads>
