@@ -53,6 +53,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kChunkBlocks = 2;
 constexpr float kRescaleSlack = 8.0f;    // base-2 units, as in the prefill kernel
 constexpr int kStreamAux = 2;            // non-temporal loads: every K/V byte is read once
+constexpr int kMergeSlots = 2 * (kWaves - 1);   // merge area slots of a workgroup (see the split kernel)
+
+// Bytes of a workgroup's merge area for g query heads of dimension d.
+inline size_t decode_merge_bytes(int g, int d) {
+    return (size_t)kMergeSlots * g * (d + 4) * 4 + (size_t)kMergeSlots * g * 4;
+}
 
 // A 64-bit value the compiler cannot prove wavefront-uniform (it came from
 // LDS) made uniform explicitly, so what derives from it stays scalar.
@@ -145,8 +151,20 @@ template <int NHB, class Rows, class Fmt>
 __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, Rows rows, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, float* __restrict__ opart, float* __restrict__ lsepart, long long* __restrict__ prefix_out,
-    int B, int Hq, int g, int P, float scale_log2, int window) {
+    int B, int Hq, int g, int P, float scale_log2, int window, int merge) {
     __shared__ long long pre[kDecodeMaxBatch + 1];
+    // Merge area (merge != 0; dynamic LDS, see decode_merge_bytes): the
+    // pieces that share a segment with a neighbouring wavefront of the
+    // workgroup, kMergeSlots slots of g rows of kD + 4 floats (normalised
+    // output; the pad spreads a store's 16 rows over the banks), then
+    // kMergeSlots x g base-2 log-sum-exps.  Slot w (w < kWaves - 1) holds
+    // the last piece of wavefront w when its segment continues into
+    // wavefront w + 1; slot kWaves - 2 + w (w >= 1) the first piece of
+    // wavefront w when its segment began in wavefront w - 1 (and does not
+    // continue past it).
+    extern __shared__ __attribute__((aligned(16))) float xm[];
+    __shared__ int xflag[kWaves];       // bit 0: slot w used; bit 1: that piece began in w - 1; bit 2: slot of the first piece used
+    __shared__ int xdst[kWaves][3];     // (b, hk, partial index) of the segment whose merge group starts at w
 
     constexpr int kD = Fmt::kD;
     constexpr int kDSteps = Fmt::kDSteps;
@@ -180,6 +198,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
         }
         if (tid == 0) pre[0] = 0;
     }
+    if (tid < kWaves) xflag[tid] = 0;
     __syncthreads();
     if (blockIdx.x == 0)
         for (int i = tid; i <= B; i += kThreads) prefix_out[i] = pre[i];
@@ -194,10 +213,12 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     const long long w = (long long)blockIdx.x * kWaves + wave;
     const long long start = w * Q;
     const long long end = min(start + Q, W);
+    // Tokens per partial result: a workgroup's four shares (merge) or one.
+    const long long Qp = merge ? Q * kWaves : Q;
+    const long long pid = merge ? (long long)blockIdx.x : w;
 
     typedef typename Fmt::template KBuf<kNB> KBuf;
     typedef typename Fmt::template VBuf<kNB> VBuf;
-    if (start >= end) return;
 
     // A piece: the part of one segment (b, hk) inside this wavefront's share,
     // tokens [p0, p1) of the segment, streamed as 32-token chunks from the
@@ -206,6 +227,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     struct Piece {
         int b, hk, p0, p1, slot, c0, nchunks;
         long long next;                     // flattened position after the piece
+        long long seg, seg_end;             // flattened range of its segment
     };
     auto describe = [&](long long pos) {
         // segment holding pos: largest b with pre[b]*Hkv <= pos
@@ -225,13 +247,15 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
         const int p1 = __builtin_amdgcn_readfirstlane((int)(min(end, S + L) - S));
         p.p0 = t_first + __builtin_amdgcn_readfirstlane((int)(pos - S));
         p.p1 = t_first + p1;
-        p.slot = __builtin_amdgcn_readfirstlane((int)(w - S / Q));  // partial index in the segment
+        p.slot = __builtin_amdgcn_readfirstlane((int)(pid - S / Qp));  // partial index in the segment
         p.c0 = p.p0 & ~15;
         p.nchunks = (p.p1 - p.c0 + kChunk - 1) / kChunk;            // >= 1
         p.next = S + p1;
+        p.seg = S;
+        p.seg_end = S + L;
         return p;
     };
-    const Piece none = {0, 0, 0, 0, 0, 0, 0, end};                  // loads nothing
+    const Piece none = {0, 0, 0, 0, 0, 0, 0, end, 0, 0};            // loads nothing
 
     // Q^T operand: lane holds Q[head hb*16 + c][32*ds + 8*q4 .. +8] (fp8
     // caches: Q[..][32*q4 + 8*ds .. +8], the order a lane's 32 contiguous K
@@ -456,7 +480,25 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
 
     // Finish a piece: each lane summed its own keys; the four lanes of a head
     // share its reference.  Lane holds head hb*16 + c, d = kPV*(4*q4 + r) + j.
+    // With merge, a piece whose segment continues into the next wavefront of
+    // the workgroup (or began in the previous one) goes to the merge area;
+    // the workgroup merges each such group after its loop and writes one
+    // partial.  A segment inside one wavefront's share of the workgroup
+    // writes its partial directly.
     auto finish = [&](const Piece& cur) {
+        const bool cross_l = merge && wave > 0 && cur.seg < start;
+        const bool cross_r = merge && wave < kWaves - 1 && cur.seg_end > end;
+        const int xs = cross_r ? wave : kWaves - 2 + wave;        // merge slot
+        if (cross_l || cross_r) {
+            if (lane == 0) {
+                xflag[wave] |= cross_r ? (1 | (cross_l ? 2 : 0)) : 4;
+                if (cross_r && !cross_l) {
+                    xdst[wave][0] = cur.b;
+                    xdst[wave][1] = cur.hk;
+                    xdst[wave][2] = cur.slot;
+                }
+            }
+        }
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             float lt = lsum[hb] + __shfl_xor(lsum[hb], 16, 64);
@@ -465,7 +507,9 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
             if (hl < g) {
                 const size_t row = ((size_t)cur.b * Hq + cur.hk * g + hl) * P + cur.slot;
                 const float inv = 1.f / lt;
-                float* dst = opart + row * kD + 4 * kPV * q4;
+                const float lse2 = ref[hb] + __builtin_amdgcn_logf(lt);   // v_log_f32: log2
+                float* dst = (cross_l || cross_r) ? xm + ((size_t)xs * g + hl) * (kD + 4) + 4 * kPV * q4
+                                                  : opart + row * kD + 4 * kPV * q4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -474,7 +518,10 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
                                          oacc[hb][j4 + 3][r] * inv};
                         *reinterpret_cast<f32x4*>(dst + kPV * r + j4) = x;
                     }
-                if (q4 == 0) lsepart[row] = ref[hb] + __builtin_amdgcn_logf(lt);   // v_log_f32: log2
+                if (q4 == 0) {
+                    if (cross_l || cross_r) xm[(size_t)kMergeSlots * g * (kD + 4) + xs * g + hl] = lse2;
+                    else lsepart[row] = lse2;
+                }
             }
         }
     };
@@ -497,31 +544,68 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
         if (ci + 1 < cur.nchunks) process(kb, vb, cur, ci + 1);
     };
 
-    Piece cur = describe(start);
-    load_q(qf, cur);
-    lookup(pha, src_of(cur, none, 0));
-    lookup(phb, src_of(cur, none, 1));
-    load(ka, va, pha, src_of(cur, none, 0));
-    for (;;) {
-        const bool more = cur.next < end;
-        const Piece nxt = more ? describe(cur.next) : none;   // none: q of head 0, no K/V
+    if (start < end) {
+        Piece cur = describe(start);
+        load_q(qf, cur);
+        lookup(pha, src_of(cur, none, 0));
+        lookup(phb, src_of(cur, none, 1));
+        load(ka, va, pha, src_of(cur, none, 0));
+        for (;;) {
+            const bool more = cur.next < end;
+            const Piece nxt = more ? describe(cur.next) : none;   // none: q of head 0, no K/V
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-            ref[hb] = -INFINITY;
-            lsum[hb] = 0.f;
+            for (int hb = 0; hb < NHB; ++hb) {
+                ref[hb] = -INFINITY;
+                lsum[hb] = 0.f;
 #pragma unroll
-            for (int j = 0; j < kPV; ++j) oacc[hb][j] = f32x4{};
+                for (int j = 0; j < kPV; ++j) oacc[hb][j] = f32x4{};
+            }
+            const int last = ((cur.nchunks + 1) & ~1) - 2;
+            for (int ci = 0; ci < last; ci += 2) pair(cur, nxt, ci, false);
+            pair(cur, nxt, last, true);
+            finish(cur);
+            if (!more) break;
+            cur = nxt;
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+                for (int ds = 0; ds < kDSteps; ++ds) qf[hb][ds] = qn[hb][ds];
         }
-        const int last = ((cur.nchunks + 1) & ~1) - 2;
-        for (int ci = 0; ci < last; ci += 2) pair(cur, nxt, ci, false);
-        pair(cur, nxt, last, true);
-        finish(cur);
-        if (!more) break;
-        cur = nxt;
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-            for (int ds = 0; ds < kDSteps; ++ds) qf[hb][ds] = qn[hb][ds];
+    }
+    if (!merge) return;
+
+    // Merge groups: a group starts at a wavefront whose last piece continues
+    // into the next wavefront and did not begin in the previous one; it holds
+    // that piece, the whole-share pieces of the wavefronts inside the segment
+    // and the first piece of the wavefront where the segment ends.  The
+    // pieces are merged in wavefront order with weights 2^(lse - max), the
+    // same rescale the combine applies across workgroups.
+    __syncthreads();
+    const float* const xlse = xm + (size_t)kMergeSlots * g * (kD + 4);
+    for (int w0 = 0; w0 < kWaves - 1; ++w0) {
+        if ((xflag[w0] & 3) != 1) continue;
+        int wl = w0 + 1;
+        while (wl < kWaves - 1 && (xflag[wl] & 3) == 3) ++wl;
+        const int nm = wl - w0 + 1;                   // pieces: slots w0 .. wl-1, then kWaves - 2 + wl
+        const size_t row0 = ((size_t)xdst[w0][0] * Hq + (size_t)xdst[w0][1] * g) * P + xdst[w0][2];
+        for (int e = tid; e < g * kD; e += kThreads) {
+            const int hl = e / kD, dd = e % kD;
+            float mx = -INFINITY;
+            for (int m = 0; m < nm; ++m) {
+                const int si = m < nm - 1 ? w0 + m : kWaves - 2 + wl;
+                mx = fmaxf(mx, xlse[si * g + hl]);
+            }
+            float den = 0.f, acc = 0.f;
+            for (int m = 0; m < nm; ++m) {
+                const int si = m < nm - 1 ? w0 + m : kWaves - 2 + wl;
+                const float wt = exp2_fast(xlse[si * g + hl] - mx);
+                den += wt;
+                acc += wt * xm[((size_t)si * g + hl) * (kD + 4) + dd];
+            }
+            const size_t row = row0 + (size_t)hl * P;
+            opart[row * kD + dd] = acc / den;
+            if (dd == 0) lsepart[row] = mx + __builtin_amdgcn_logf(den);
+        }
     }
 }
 
@@ -538,7 +622,7 @@ constexpr int kCombineFewPartials = 32;  // at most this many per row: one wavef
 template <int kD>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ lsepart, const long long* __restrict__ prefix,
-    uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW) {
+    uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW, int per) {
     constexpr int kE = kD / 64;          // output elements per lane: d = kE * lane ..
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
@@ -548,7 +632,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     float m = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f;
     if (L > 0) {
         const long long W = prefix[B] * Hkv;
-        const long long Q = share_tokens(W, NW);
+        const long long Q = share_tokens(W, NW) * per;      // tokens per partial
         const long long S = prefix[b] * Hkv + (long long)(hq / g) * L;
         const int np = (int)((S + L - 1) / Q - S / Q) + 1;
         const size_t row0 = ((size_t)b * Hq + hq) * P;
@@ -599,7 +683,7 @@ constexpr int kWideBatch = 8;
 template <int kD>
 __global__ __launch_bounds__(256) void decode_combine_wide_kernel(
     const float* __restrict__ opart, const float* __restrict__ lsepart, const long long* __restrict__ prefix,
-    uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW) {
+    uint16_t* __restrict__ o, int B, int Hq, int g, int P, long long NW, int per) {
     constexpr int kCols = kD / 4;
     constexpr int kGroups = 256 / kCols;
     __shared__ f32x4 red_acc[kGroups][kCols];
@@ -614,7 +698,7 @@ __global__ __launch_bounds__(256) void decode_combine_wide_kernel(
     f32x4 acc = f32x4{};
     if (L > 0) {
         const long long W = prefix[B] * Hkv;
-        const long long Q = share_tokens(W, NW);
+        const long long Q = share_tokens(W, NW) * per;      // tokens per partial
         const long long S = prefix[b] * Hkv + (long long)(hq / g) * L;
         const int np = (int)((S + L - 1) / Q - S / Q) + 1;
         const size_t row0 = ((size_t)b * Hq + hq) * P;
@@ -680,18 +764,31 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
     long long* prefix = reinterpret_cast<long long*>(base + ws.prefix);
     const int P = decode_max_partials(a.max_seq_len);
     const int g = a.Hq / a.Hkv;
-    hipLaunchKernelGGL((decode_split_kernel<NHB, Rows, Fmt>), dim3(nwg), dim3(kThreads), 0, stream,
+    // Merge within workgroups when the merge area fits beside the prefix
+    // sums without lowering the number of resident workgroups.
+    const size_t xbytes = decode_merge_bytes(g, kD);
+    const size_t lds_budget = (size_t)160 * 1024 / (NHB == 1 ? 2 : 1);
+    const size_t static_lds = (size_t)(kDecodeMaxBatch + 1) * 8 + 1024;
+    const int merge = xbytes + static_lds <= lds_budget ? 1 : 0;
+    auto kernel = decode_split_kernel<NHB, Rows, Fmt>;
+    if (merge && xbytes > 64 * 1024) {       // above the default dynamic LDS limit
+        const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    (int)(lds_budget - static_lds));
+        if (attr != hipSuccess) return attr;
+    }
+    hipLaunchKernelGGL(kernel, dim3(nwg), dim3(kThreads), merge ? xbytes : 0, stream,
                        static_cast<const uint16_t*>(a.q), rows, a.block_table, a.seq_lens, opart, lsepart, prefix, a.B,
-                       a.Hq, g, P,
-                       a.scale * kLog2e, a.window > 0 ? a.window : 0);
+                       a.Hq, g, P, a.scale * kLog2e, a.window > 0 ? a.window : 0, merge);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int per = merge ? kWaves : 1;
     if (P <= kCombineFewPartials)
         hipLaunchKernelGGL((decode_combine_kernel<kD>), dim3(a.Hq, a.B), dim3(64), 0, stream, opart, lsepart,
-                           prefix, static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
+                           prefix, static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves, per);
     else
         hipLaunchKernelGGL((decode_combine_wide_kernel<kD>), dim3(a.Hq, a.B), dim3(256), 0, stream, opart, lsepart,
-                           prefix, static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves);
+                           prefix, static_cast<uint16_t*>(a.o), a.B, a.Hq, g, P, (long long)nwg * kWaves, per);
     return hipGetLastError();
 }
 
