@@ -582,30 +582,51 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_split_kerne
     // same rescale the combine applies across workgroups.
     __syncthreads();
     const float* const xlse = xm + (size_t)kMergeSlots * g * (kD + 4);
+    // The groups (at most kWaves - 1): first wavefront and piece count.
+    int gw0[kWaves - 1], gnm[kWaves - 1], ng = 0;
+#pragma unroll
     for (int w0 = 0; w0 < kWaves - 1; ++w0) {
         if ((xflag[w0] & 3) != 1) continue;
         int wl = w0 + 1;
         while (wl < kWaves - 1 && (xflag[wl] & 3) == 3) ++wl;
-        const int nm = wl - w0 + 1;                   // pieces: slots w0 .. wl-1, then kWaves - 2 + wl
-        const size_t row0 = ((size_t)xdst[w0][0] * Hq + (size_t)xdst[w0][1] * g) * P + xdst[w0][2];
-        for (int e = tid; e < g * kD; e += kThreads) {
-            const int hl = e / kD, dd = e % kD;
-            float mx = -INFINITY;
-            for (int m = 0; m < nm; ++m) {
-                const int si = m < nm - 1 ? w0 + m : kWaves - 2 + wl;
-                mx = fmaxf(mx, xlse[si * g + hl]);
-            }
-            float den = 0.f, acc = 0.f;
-            for (int m = 0; m < nm; ++m) {
-                const int si = m < nm - 1 ? w0 + m : kWaves - 2 + wl;
-                const float wt = exp2_fast(xlse[si * g + hl] - mx);
-                den += wt;
-                acc += wt * xm[((size_t)si * g + hl) * (kD + 4) + dd];
-            }
-            const size_t row = row0 + (size_t)hl * P;
-            opart[row * kD + dd] = acc / den;
-            if (dd == 0) lsepart[row] = mx + __builtin_amdgcn_logf(den);
+        gw0[ng] = w0;
+        gnm[ng] = wl - w0 + 1;          // pieces: slots w0 .. wl-1, then kWaves - 2 + wl
+        ++ng;
+    }
+    // One unit = 16 consecutive elements of one head's row: its weights are
+    // formed once, the rows are read and written 16 bytes at a time.
+    constexpr int kUnitsPerRow = kD / 16;
+    const int units = g * kUnitsPerRow;
+    for (int u = tid; u < ng * units; u += kThreads) {
+        const int gi = u / units, r = u - gi * units;
+        const int hl = r / kUnitsPerRow, d0 = 16 * (r % kUnitsPerRow);
+        const int w0 = gw0[gi], nm = gnm[gi];
+        int si[kWaves];
+        float lv[kWaves], mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < kWaves; ++m) {
+            si[m] = m < nm - 1 ? w0 + m : kWaves - 2 + w0 + nm - 1;
+            lv[m] = m < nm ? xlse[si[m] * g + hl] : -INFINITY;
+            mx = fmaxf(mx, lv[m]);
         }
+        float wt[kWaves], den = 0.f;
+#pragma unroll
+        for (int m = 0; m < kWaves; ++m) {
+            wt[m] = m < nm ? exp2_fast(lv[m] - mx) : 0.f;
+            den += wt[m];
+        }
+        const float inv = 1.f / den;
+        const size_t row = ((size_t)xdst[w0][0] * Hq + (size_t)xdst[w0][1] * g + hl) * P + xdst[w0][2];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int m = 0; m < kWaves; ++m)
+                if (m < nm)
+                    acc += wt[m] * *reinterpret_cast<const f32x4*>(xm + ((size_t)si[m] * g + hl) * (kD + 4) + d0 + 4 * c4);
+            *reinterpret_cast<f32x4*>(opart + row * kD + d0 + 4 * c4) = acc * inv;
+        }
+        if (d0 == 0) lsepart[row] = mx + __builtin_amdgcn_logf(den);
     }
 }
 
