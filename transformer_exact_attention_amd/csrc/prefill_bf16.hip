@@ -388,6 +388,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < kDSteps; ++t) qk_step(k_s0, scur, t, t == 0);
 
+    // Reference of the first tile: its largest visible score (the largest of
+    // the lane pair's 32 keys per query column), so that the first step
+    // needs no rescaling pass; a column with no visible key in the tile keeps
+    // -inf and takes that pass, as any later tile whose sum exceeds the bound.
+    // The score MFMAs must have finished before their results are read.
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(scur[nb][kb]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(scur[nb][kb]));
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        float tm = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+                const bool hidden = kWindow ? (uint32_t)(my_last[nb] - key) >= (uint32_t)window : key > my_last[nb];
+                tm = hidden ? tm : fmaxf(tm, scur[nb][kb][e]);
+            }
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        ref[nb] = tm * scale_log2;
+    }
+
     // Operands of one 4-MFMA group of the pipelined step.  A score group
     // (QK, d-step t) reads K rows n and 32+n of d-chunk 2t+hh (two LDS
     // reads); a P.V group reads the transposed V fragments of two d-tiles
