@@ -611,7 +611,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 pcur[nb][s4] = __builtin_bit_cast(bf16x8, u32x4{pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]});
             }
 
-        // Rare: some p exceeded the bound (or this is the first tile).  Redo
+        // Rare: some p exceeded the bound (or a column has seen no visible key
+        // yet, so its reference is still -inf).  Redo
         // the tile against its true max and rescale what came before.
         const bool over = !(psum[0] <= kSumLimit) || !(psum[1] <= kSumLimit);
         if (__builtin_amdgcn_ballot_w64(over)) {
