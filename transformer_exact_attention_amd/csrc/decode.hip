@@ -15,9 +15,11 @@
 // one per wavefront, and exactly as many wavefronts are launched as the GPU
 // holds at once: every wavefront streams the same number of bytes, whatever
 // the length mix.  A share crossing segment boundaries (a segment = one K/V
-// head of one sequence) is processed piece by piece; each piece ends in one
+// head of one sequence) is processed piece by piece; each piece ends in a
 // partial result (normalised output + base-2 log-sum-exp for the g query
-// heads of the group).  The wavefront streams 32-token chunks, double-buffered
+// heads of the group), and the pieces a segment has in the four shares of
+// one workgroup are merged in LDS, so a segment gets one partial per
+// workgroup it meets.  The wavefront streams 32-token chunks, double-buffered
 // across its whole share: chunk i+1 is loaded (non-temporal, range-checked
 // buffer loads, no branches) while chunk i is computed, and the next piece's
 // first chunk and Q fragments are fetched while the current piece finishes;

@@ -58,7 +58,8 @@ struct DecodeArgs {
 // triples, W = sum_b seq_lens[b] * Hkv tokens, is cut into equal consecutive
 // shares of Q tokens, one per wavefront (Q >= kDecodeMinShare, a multiple of
 // 16).  A share covering part of a (sequence, K/V head) segment produces one
-// partial result for that segment, so a segment of length L has at most
+// partial result for that segment (merged per workgroup of four shares where
+// the workgroup has room for it), so a segment of length L has at most
 // ceil(L / kDecodeMinShare) + 1 partials.
 constexpr int kDecodeMinShare = 256;
 constexpr int kDecodeMaxBatch = 4096;     // sequence prefix sums live in LDS
