@@ -788,11 +788,15 @@ hipError_t launch_both(const DecodeArgs& a, const Rows& rows, hipStream_t stream
     const int P = decode_max_partials(a.max_seq_len);
     const int g = a.Hq / a.Hkv;
     // Merge within workgroups when the merge area fits beside the prefix
-    // sums without lowering the number of resident workgroups.
+    // sums without lowering the number of resident workgroups (the CU's LDS,
+    // 160 KB on gfx950, shared by the resident workgroups).
     const size_t xbytes = decode_merge_bytes(g, kD);
-    const size_t lds_budget = (size_t)160 * 1024 / (NHB == 1 ? 2 : 1);
+    int lds_cu = 0;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+        lds_cu = 0;                                                   // unknown: no merge
+    const size_t lds_budget = (size_t)lds_cu / (NHB == 1 ? 2 : 1);
     const size_t static_lds = (size_t)(kDecodeMaxBatch + 1) * 8 + 1024;
-    const int merge = xbytes + static_lds <= lds_budget ? 1 : 0;
+    const int merge = lds_budget > static_lds && xbytes <= lds_budget - static_lds ? 1 : 0;
     auto kernel = decode_split_kernel<NHB, Rows, Fmt>;
     if (merge && xbytes > 64 * 1024) {       // above the default dynamic LDS limit
         const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
