@@ -188,16 +188,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // is given the contiguous item range [x * N/8, (x+1) * N/8): whole planes,
     // whose K/V then stay in that XCD's L2 instead of being fetched by all 8.
     // With by_cost (planes too short to fill an XCD), the XCD's items are
-    // handed out heaviest query block first across all of its planes, so the
-    // CUs that start with light items do not meet heavy ones at the end.
+    // handed out heaviest query block first across a group of its planes
+    // (four, when the XCD's plane count divides by four; whose K/V, 1 MB
+    // each at S = 2048, stay in the XCD's 4 MB L2), group after group, so
+    // the CUs that start with light items do not meet heavy ones at the end.
     const int nitems = (int)gridDim.x;
     const int L = (int)blockIdx.x;
     int plane, qb;
     if (by_cost) {
         const int ppx = nitems / (8 * nqb);               // planes per XCD
         const int j = L >> 3;
-        plane = (L & 7) * ppx + j % ppx;
-        qb = nqb - 1 - j / ppx;
+        const int G = (ppx % 4) == 0 ? 4 : ppx;           // planes dealt together
+        const int grp = j / (G * nqb), jj = j - grp * (G * nqb);
+        plane = (L & 7) * ppx + grp * G + jj % G;
+        qb = nqb - 1 - jj / G;
     } else {
         const int item = (nitems & 7) == 0 ? (L & 7) * (nitems >> 3) + (L >> 3) : L;
         plane = item / nqb;
