@@ -204,3 +204,32 @@ def test_full_size_prefill_sampled(ga, cfg):
             w_, _ = assert_close(got, ref, "bf16", f"{w.name} b{b} h{hq}")
             worst = max(worst, w_)
     note(f"{w.name}: worst sampled abs err {worst:.3e}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("window", [None, 4096])
+def test_long_context_32k_sampled(ga, window):
+    # LLaMA-3-8B-shaped attention (32 query heads, 8 K/V heads, d 128) at the
+    # 32K context the pages discuss for it [Attention variants deep-dive, §8
+    # Q4], causal and with a 4096-key sliding window: 512 key tiles per row
+    # block, planes far longer than an XCD's share of the grid.
+    import torch
+    B, Hq, Hkv, S, d = 1, 32, 8, 32768, 128
+    q = W.normal([7400, 0], (B, Hq, S, d), "bf16")
+    k = W.normal([7400, 1], (B, Hkv, S, d), "bf16")
+    v = W.normal([7400, 2], (B, Hkv, S, d), "bf16")
+    note(f"prefill 32K context window={window}")
+    qt, kt, vt = to_gpu(q, "bf16"), to_gpu(k, "bf16"), to_gpu(v, "bf16")
+    o = torch.full_like(qt, float("nan"))
+    ga.attn_prefill_fwd(qt, kt, vt, o, causal=True, window=window)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    of = o.view(torch.int16).cpu().numpy()
+    rng = np.random.default_rng(7400 + (window or 0))
+    for hq in range(0, Hq, 3):
+        rows = sample_rows(S, rng)
+        hk = oracle.kv_head_index(hq, Hq, Hkv)
+        ref, _ = oracle.attention_rows(ref_f64(q[:, hq:hq + 1], "bf16"), ref_f64(k[:, hk:hk + 1], "bf16"),
+                                       ref_f64(v[:, hk:hk + 1], "bf16"), 0, 0, rows, None, True, window)
+        got = ref_f64(of[0, hq, rows].view(np.uint16), "bf16")
+        assert_close(got, ref, "bf16", f"32K window={window} h{hq}")
