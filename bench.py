@@ -53,9 +53,10 @@ def parse():
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload separately (one JSON line each) instead of the step")
-    ap.add_argument("--sweep-kinds", default="prefill,decode,kv,fp8,window,bwd",
-                    help="comma list of the sweep's parts: prefill, decode, kv (paged KV-cache writes), "
-                         "fp8 (decode over fp8 caches), window (sliding-window prefill and decode)")
+    ap.add_argument("--sweep-kinds", default="prefill,long,decode,kv,fp8,window,bwd",
+                    help="comma list of the sweep's parts: prefill, long (32K-context GQA prefill), decode, "
+                         "kv (paged KV-cache writes), fp8 (decode over fp8 caches), window (sliding-window "
+                         "prefill and decode), bwd (backward)")
     return ap.parse_args()
 
 
@@ -119,8 +120,9 @@ def cpu_baseline_prefill(w, q, k, v, budget_s=12.0):
 
 
 def sweep(args):
-    """Every workload on its own: prefill (fp32 tiny, MHA S2048, GQA S8192), contiguous
-    decode, paged decode with Hkv in {32, 8, 1}.  One JSON line per workload."""
+    """Every workload on its own: prefill (fp32 tiny, MHA S2048, GQA S8192, and the
+    32K-context GQA point), contiguous decode, paged decode with Hkv in {32, 8, 1}, and
+    the parts chosen by --sweep-kinds.  One JSON line per workload."""
     import torch
     from transformer_exact_attention_amd import gqa_attn
     from transformer_exact_attention_amd import workloads as W
@@ -146,7 +148,9 @@ def sweep(args):
 
     kinds = set(args.sweep_kinds.split(","))
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    for w in (W.CFG1, W.CFG2, W.CFG3) if "prefill" in kinds else ():
+    prefill_points = ((W.CFG1, W.CFG2, W.CFG3) if "prefill" in kinds else ()) + \
+        ((W.LONG_CONTEXT,) if "long" in kinds else ())
+    for w in prefill_points:
         log(f"sweep {w.name}")
         q, k, v = (gpu(x, w.dtype) for x in W.prefill_inputs(w))
         o = torch.empty_like(q)

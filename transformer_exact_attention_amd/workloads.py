@@ -168,6 +168,12 @@ def cfg5(Hkv: int) -> DecodeWorkload:
                           8192, 32768, True)
 
 
+# Long context: LLaMA-3-8B-shaped attention (32 query heads, 8 K/V heads,
+# d 128) at 32K positions [Attention variants deep-dive, §8 Q4]; a sweep
+# point beside the prefill workloads, not a parity configuration.
+LONG_CONTEXT = PrefillWorkload("gqa_causal_prefill_B1_Hq32_Hkv8_S32768_d128", 6, 1, 32, 8, 32768, 32768, 128,
+                               "bf16", True)
+
 PREFILL_WORKLOADS = {1: CFG1, 2: CFG2, 3: CFG3}
 DECODE_WORKLOADS = {4: CFG4, "5_hkv32": cfg5(32), "5_hkv8": cfg5(8), "5_hkv1": cfg5(1)}
 
