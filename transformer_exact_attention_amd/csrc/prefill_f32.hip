@@ -67,19 +67,36 @@ __global__ __launch_bounds__(kThreadsF32) void prefill_f32_kernel(
     const int my_last = causal ? row + (Sk - Sq) : Sk - 1;
     const int kbeg = kWindow ? max(0, row0 + (Sk - Sq) - window + 1) / kKeysF32 * kKeysF32 : 0;
 
-    for (int j0 = kbeg; j0 < kend; j0 += kKeysF32) {
-        __syncthreads();
-        for (int e = tid; e < kKeysF32 * D / 4; e += kThreadsF32) {
+    // The next tile's K and V rows are loaded into registers while the
+    // current tile is computed (its LDS copy is written at the top of the
+    // next iteration), so a tile's load latency is paid once per row block,
+    // not once per tile.
+    constexpr int kPer = kKeysF32 * D / 4 / kThreadsF32;   // float4 of K (and of V) per thread
+    float4 nk[kPer], nv[kPer];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            const int e = x * kThreadsF32 + tid;
             const int r = e / (D / 4), c = 4 * (e % (D / 4));
             const bool in = (j0 + r) < Sk;
-            const float4 kz = in ? *reinterpret_cast<const float4*>(k + kvoff + (size_t)(j0 + r) * D + c)
-                                 : float4{0.f, 0.f, 0.f, 0.f};
-            const float4 vz = in ? *reinterpret_cast<const float4*>(v + kvoff + (size_t)(j0 + r) * D + c)
-                                 : float4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<float4*>(&ks[r][c]) = kz;
-            *reinterpret_cast<float4*>(&vs[r][c]) = vz;
+            nk[x] = in ? *reinterpret_cast<const float4*>(k + kvoff + (size_t)(j0 + r) * D + c)
+                       : float4{0.f, 0.f, 0.f, 0.f};
+            nv[x] = in ? *reinterpret_cast<const float4*>(v + kvoff + (size_t)(j0 + r) * D + c)
+                       : float4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    if (kbeg < kend) fetch(kbeg);
+    for (int j0 = kbeg; j0 < kend; j0 += kKeysF32) {
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            const int e = x * kThreadsF32 + tid;
+            const int r = e / (D / 4), c = 4 * (e % (D / 4));
+            *reinterpret_cast<float4*>(&ks[r][c]) = nk[x];
+            *reinterpret_cast<float4*>(&vs[r][c]) = nv[x];
         }
         __syncthreads();
+        if (j0 + kKeysF32 < kend) fetch(j0 + kKeysF32);
 
         float s[kKeysF32];
         float tmax = -INFINITY;
